@@ -1,0 +1,278 @@
+"""Bench for fused candidate scoring on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the whole hot path (similarity + in-workgroup softmax)
+over one batch: the 1024-question Kev-shaped batch (dot, K=255, D=2560, fp32,
+2.67 GB of candidates), inputs resident in HBM before the timed region.
+Timing uses HIP events on the stream the kernel runs on, around K
+back-to-back calls issued from native code. Prints ONE JSON line.
+
+Beside the headline it reports (same line):
+  * roofline: algorithmic bytes per launch / event-timed launch duration
+    against the 8 TB/s HBM peak, and the HBM traffic measured by rocprofv3
+    counters when the committed profile matches the current kernel source;
+  * latency: single-question and small-batch calls timed through hipGraph
+    replay (2000 replays of a one-node graph, the page's protocol) next to an
+    empty kernel of the same grid and block replayed the same way: the launch
+    floor;
+  * cpu_baseline: the double-precision oracle on the host, single-threaded,
+    over the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = ROOT / "candidate_scoring_amd" / "csrc" / "cs_kernels.hip"
+TRAFFIC_PROFILE = ROOT / "profiles" / "fused_regq_kev_batch1024_255x2560_traffic.md"
+LATENCY_CONFIGS = ["clm_cos_5x512", "clm_cos_255x512", "clm_cos_batch8_255x512",
+                   "kev_dot_255x2560"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha256() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch from the committed counter profile, or None when
+    it is missing or was taken on a different kernel source."""
+    if not TRAFFIC_PROFILE.exists():
+        return None
+    text = TRAFFIC_PROFILE.read_text()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_tr or m_sha.group(1) != source_sha256():
+        return None
+    return float(m_tr.group(1))
+
+
+class Device:
+    def __init__(self):
+        import torch
+
+        import candidate_scoring_amd as cs
+
+        self.torch = torch
+        self.cs = cs
+        cs.load()
+        self.bench = cs.load_bench()
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+
+    def upload(self, w):
+        t = self.torch
+        q = t.from_numpy(w.Q).to(self.dev)
+        c = t.from_numpy(w.C).to(self.dev)
+        out = t.empty((w.B, w.K), dtype=t.float32, device=self.dev)
+        return q, c, out
+
+    def call(self, w, q, c, out, use_workspace=True, groups=0):
+        cs = self.cs
+        ws, nbytes = None, 0
+        if groups > 0:
+            nbytes = cs.cs_workspace_bytes_for_groups(w.B, groups)
+        elif use_workspace:
+            nbytes = cs.cs_workspace_bytes(w.B, w.K, w.D, w.similarity)
+        if nbytes:
+            ws = self.torch.zeros(nbytes, dtype=self.torch.uint8, device=self.dev)
+        call = cs.CsbCall(q.data_ptr(), c.data_ptr(), out.data_ptr(), w.B, w.K, w.D,
+                          cs._sim(w.similarity), float(w.scale), float(w.temperature),
+                          ws.data_ptr() if ws is not None else None, nbytes, groups)
+        return call, ws
+
+    def time_calls(self, call, iters) -> float:
+        ms = ctypes.c_float()
+        st = self.bench.csb_time_calls(ctypes.byref(call), iters, self.stream.cuda_stream,
+                                       ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"csb_time_calls failed: {st}")
+        return ms.value
+
+    def time_graph(self, call, replays, warmup=20):
+        ms, nodes = ctypes.c_float(), ctypes.c_size_t()
+        st = self.bench.csb_time_graph(ctypes.byref(call), 1, replays, warmup, ctypes.byref(ms),
+                                       ctypes.byref(nodes))
+        if st != 0:
+            raise RuntimeError(f"csb_time_graph failed: {st}")
+        return ms.value, nodes.value
+
+    def time_empty(self, grid, block, iters, graph):
+        ms = ctypes.c_float()
+        st = self.bench.csb_time_empty(grid, block, iters, int(graph), 1,
+                                       self.stream.cuda_stream, ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"csb_time_empty failed: {st}")
+        return ms.value
+
+
+def latency_section(devc, replays):
+    cs = devc.cs
+    res = {}
+    for name in LATENCY_CONFIGS:
+        w = workloads.make(name)
+        q, c, out = devc.upload(w)
+        row = {"B": w.B, "K": w.K, "D": w.D, "similarity": w.similarity}
+        for label, use_ws in (("split", True), ("one_wg_per_question", False)):
+            call, _ws = devc.call(w, q, c, out, use_workspace=use_ws)
+            devc.time_calls(call, 50)
+            g_ms, nodes = devc.time_graph(call, replays)
+            d_ms = devc.time_calls(call, replays)
+            st, grid, block, G = cs.cs_plan_launch(w.B, w.K, w.D, w.similarity, use_ws)
+            assert st == 0
+            f_ms = devc.time_empty(grid, block, replays, True)
+            row[label] = {"groups": G, "grid": grid, "block": block,
+                          "graph_us_per_call": round(1e3 * g_ms / replays, 3),
+                          "direct_us_per_call": round(1e3 * d_ms / replays, 3),
+                          "graph_nodes": nodes,
+                          "empty_kernel_graph_floor_us": round(1e3 * f_ms / replays, 3)}
+        res[name] = row
+        log(f"latency {name}: {row}")
+        del q, c, out
+    return res
+
+
+def cpu_baseline(w, max_seconds=30.0):
+    """The oracle as it stands, single-threaded, on the headline batch: as
+    many whole passes as fit in about max_seconds (at least one)."""
+    import oracle
+
+    orc = oracle.load()
+    reps, total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        orc.score(w.Q, w.C, w.similarity, w.scale, w.temperature)
+        total += time.perf_counter() - t0
+        reps += 1
+        if total * (reps + 1) / reps > max_seconds or reps >= 3:
+            break
+    per_call = total / reps
+    return {"value": round(w.algorithmic_bytes / per_call / 1e9, 3), "unit": "GB/s",
+            "us_per_call": round(per_call * 1e6, 1), "cores": 1, "kind": "oracle",
+            "sample": f"all {w.B} questions of the headline batch, {reps} pass(es), "
+                      f"single-threaded C float64 oracle",
+            "cpu": cpu_model(), "host_cores_available": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replays", type=int, default=2000, help="graph replays per latency figure")
+    ap.add_argument("--no-latency", action="store_true", help="skip the small-shape latencies")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(questions would shard across GPUs with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    devc = Device()
+    torch = devc.torch
+    w = workloads.make(workloads.HEADLINE)
+    log(f"headline: {w.name} B={w.B} K={w.K} D={w.D} bytes={w.algorithmic_bytes}")
+    q, c, out = devc.upload(w)
+    call, _ws = devc.call(w, q, c, out)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device=devc.dev)
+        dst = torch.empty_like(src)
+        st = devc.bench.csb_copy(src.data_ptr(), dst.data_ptr(), n, devc.stream.cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+        del src, dst
+
+    if args.warmup:
+        devc.time_calls(call, args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_ms = devc.time_calls(call, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_s = ev_ms / 1e3 / args.steps
+    gbs = w.algorithmic_bytes / per_launch_s / 1e9
+    log(f"headline: {1e6 * per_launch_s:.1f} us/call, {gbs:.1f} GB/s "
+        f"(wall {wall:.3f} s for {args.steps} steps)")
+
+    # spot parity of the timed launch configuration (first and last question)
+    import oracle
+
+    orc = oracle.load()
+    got = out.cpu().numpy()
+    for b in (0, w.B - 1):
+        want = orc.score(w.Q[b], w.C[b], w.similarity, w.scale, w.temperature)
+        err = float(np.max(np.abs(got[b].astype(np.float64) - want)))
+        if not err <= 1e-4:
+            raise SystemExit(f"parity failure on question {b}: {err}")
+    del q, c, out
+
+    traffic = committed_traffic()
+    result = {
+        "metric": "µs/call + achieved HBM GB/s, fused score+softmax, K=255 D=512 and D=2560",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "us_per_call": round(1e6 * per_launch_s, 2),
+        "questions_per_s": round(w.B / per_launch_s, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * per_launch_s, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,1) fp32 queries and candidates",
+        "config": {"workload": "batch of 1024 questions, dot similarity (Kev), K=255, D=2560, "
+                               "scale 1/16, T=1, fp32, one launch",
+                   "global_batch": w.B, "K": w.K, "D": w.D, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "fused_regq<dot, nv=10, rows=2, full>",
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+    }
+    if not args.no_latency:
+        result["latency"] = latency_section(devc, args.replays)
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the headline batch")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,76 @@
+"""Builds the HIP libraries in-tree for gfx950 with hipcc.
+
+    python -m candidate_scoring_amd.build
+
+produces ``candidate_scoring_amd/libcs.so`` (the C ABI of
+include/candidate_scoring.h) and ``candidate_scoring_amd/libcs_bench.so``
+(native timing helpers for bench.py).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIBRARY = PKG / "libcs.so"
+BENCH_LIBRARY = PKG / "libcs_bench.so"
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def common_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-Wall",
+        # keep the compiler from emitting packed fp32 math (v_pk_*_f32)
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{INCLUDE}",
+        f"-I{CSRC}",
+    ]
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"build failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> list[Path]:
+    cc = hipcc()
+    tmp = LIBRARY.with_suffix(".so.tmp")
+    _run([cc, *common_flags(), "-o", str(tmp), str(CSRC / "cs_kernels.hip"),
+          str(CSRC / "cs_api.cpp")], verbose)
+    tmp.replace(LIBRARY)
+    tmpb = BENCH_LIBRARY.with_suffix(".so.tmp")
+    _run([cc, *common_flags(), "-o", str(tmpb), str(CSRC / "cs_bench.hip"),
+          f"-L{PKG}", "-lcs", "-Wl,-rpath,$ORIGIN"], verbose)
+    tmpb.replace(BENCH_LIBRARY)
+    return [LIBRARY, BENCH_LIBRARY]
+
+
+if __name__ == "__main__":
+    for p in build(verbose=True):
+        print("built", p)

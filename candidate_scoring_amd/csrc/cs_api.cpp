@@ -1,0 +1,233 @@
+// cs_api.cpp -- the C ABI declared in include/candidate_scoring.h:
+// argument validation, launch planning and the one launch per call.
+//
+// Source: pull request "cuda: add a fused candidate-scoring kernel for CLM
+// and Kev", "Verified on hardware": the single-question and batch entry
+// points must agree; K above 255, K of zero, D of zero, a zero scale, a
+// negative temperature and a null query are errors, not scored answers; the
+// call queues on the caller's stream and never synchronizes, and a capture
+// of it holds exactly one node.
+
+#include "candidate_scoring.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "cs_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 4;
+// Workgroups a small batch is spread over: two per CU on a 256-CU MI355X.
+constexpr int kSplitTarget = 512;
+// Questions at or above which a batch already fills the chip on its own.
+constexpr int kSplitMaxB = 256;
+// Grid cap; items beyond it are strided over the resident workgroups.
+constexpr long long kGridCap = 1 << 20;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t ticket_bytes(int B) { return align_up(sizeof(uint32_t) * (size_t)B, 256); }
+
+size_t workspace_for(int B, int G) {
+  if (G <= 1) return 0;
+  return ticket_bytes(B) + sizeof(float) * 2 * (size_t)B * (size_t)G;
+}
+
+int validate(const void* q, const void* c, const void* out, long long B, long long K,
+             long long D, int sim, float scale, float temperature) {
+  if (q == nullptr || c == nullptr || out == nullptr) return CS_ERR_NULL_POINTER;
+  if (B < 1) return CS_ERR_BATCH;
+  if (K < 1 || K > CS_MAX_K) return CS_ERR_K_RANGE;
+  if (D < 1) return CS_ERR_D_RANGE;
+  if (sim != CS_SIM_DOT && sim != CS_SIM_COSINE) return CS_ERR_SIMILARITY;
+  if (scale == 0.0f || isnan(scale) || isinf(scale)) return CS_ERR_SCALE;
+  if (!(temperature > 0.0f) || isinf(temperature)) return CS_ERR_TEMPERATURE;
+  return CS_OK;
+}
+
+// Optional check (CS_DEBUG_POINTERS=1) that a pointer is device memory.
+bool debug_pointers() {
+  static const bool on = [] {
+    const char* v = getenv("CS_DEBUG_POINTERS");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
+
+bool is_device_pointer(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+int plan_groups(int B, int K) {
+  if (B >= kSplitMaxB || K == 1) return 1;
+  int G = std::min(K, (kSplitTarget + B - 1) / B);
+  const int rpg = (K + G - 1) / G;
+  return (K + rpg - 1) / rpg;  // no empty slices
+}
+
+// Launch shape for a validated call: kernel variant from D and alignment,
+// up to four waves per workgroup (enough for the slice's rows).
+cs::LaunchShape make_shape(int B, int K, int D, int G, int rpg, const void* Q, const void* C) {
+  (void)K;
+  cs::LaunchShape ls;
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(Q) & 15u) == 0 &&
+                         (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+  const bool vec4 = (D % 4 == 0) && aligned16;
+  ls.nv = vec4 ? cs::regq_nv_for(D) : 0;
+  ls.vec = vec4 ? 4 : 1;
+  const int rows_per_wave = ls.nv > 0 ? cs::regq_rows_per_wave(ls.nv) : 4;
+  const int waves = std::max(1, std::min(kMaxWaves, (rpg + rows_per_wave - 1) / rows_per_wave));
+  ls.block = (unsigned)(waves * kWave);
+  ls.grid = (unsigned)std::min<long long>((long long)B * G, kGridCap);
+  return ls;
+}
+
+int score(const float* Q, const float* C, int B, int K, int D, int sim, float scale,
+          float temperature, float* out, void* ws, size_t ws_bytes, int groups,
+          hipStream_t stream) {
+  int st = validate(Q, C, out, B, K, D, sim, scale, temperature);
+  if (st != CS_OK) return st;
+  if (groups < 1 || groups > K) return CS_ERR_WORKSPACE;
+  const int rpg = (K + groups - 1) / groups;
+  const int G = (K + rpg - 1) / rpg;
+  if (G != groups) return CS_ERR_WORKSPACE;  // would leave a slice empty
+  if (G > 1) {
+    if (ws == nullptr || ws_bytes < workspace_for(B, G) ||
+        (reinterpret_cast<uintptr_t>(ws) & 7u) != 0)
+      return CS_ERR_WORKSPACE;
+  }
+  if (debug_pointers()) {
+    if (!is_device_pointer(Q) || !is_device_pointer(C) || !is_device_pointer(out) ||
+        (G > 1 && !is_device_pointer(ws)))
+      return CS_ERR_HOST_POINTER;
+  }
+
+  cs::KernelArgs a;
+  a.Q = Q;
+  a.C = C;
+  a.out = out;
+  a.tickets = G > 1 ? static_cast<unsigned*>(ws) : nullptr;
+  a.partials = G > 1 ? reinterpret_cast<float2*>(static_cast<char*>(ws) + ticket_bytes(B))
+                     : nullptr;
+  a.B = B;
+  a.K = K;
+  a.D = D;
+  a.G = G;
+  a.rpg = rpg;
+  // scale / T rounded once to fp32 from the exact double quotient.
+  a.zscale = (float)((double)scale / (double)temperature);
+  a.cosine = sim == CS_SIM_COSINE;
+
+  const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, Q, C);
+  const hipError_t err = cs::launch_fused(a, ls, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return CS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cs_abi_version(void) { return CS_ABI_VERSION; }
+
+const char* cs_status_string(int status) {
+  switch (status) {
+    case CS_OK: return "ok";
+    case CS_ERR_NULL_POINTER: return "null query, candidates or output pointer";
+    case CS_ERR_K_RANGE: return "candidate count K must be in 1..255";
+    case CS_ERR_D_RANGE: return "vector length D must be at least 1";
+    case CS_ERR_SCALE: return "scale must be finite and nonzero";
+    case CS_ERR_TEMPERATURE: return "temperature must be finite and positive";
+    case CS_ERR_BATCH: return "batch size B must be at least 1";
+    case CS_ERR_SIMILARITY: return "similarity must be CS_SIM_DOT or CS_SIM_COSINE";
+    case CS_ERR_WORKSPACE: return "workspace missing, too small or misaligned, or bad group count";
+    case CS_ERR_LAUNCH: return "kernel launch failed";
+    case CS_ERR_HOST_POINTER: return "a pointer argument is not device memory";
+    default: return "unknown status";
+  }
+}
+
+int cs_last_hip_error(void) { return g_last_hip_error; }
+
+int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace) {
+  if (validate(&B, &B, &B, B, K, D, similarity, 1.0f, 1.0f) != CS_OK) return 0;
+  return has_workspace ? plan_groups(B, K) : 1;
+}
+
+int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
+                   unsigned* grid, unsigned* block, int* groups) {
+  const int G = cs_plan_groups(B, K, D, similarity, has_workspace);
+  if (G < 1) return CS_ERR_K_RANGE;
+  const int rpg = (K + G - 1) / G;
+  // 16-byte aligned or deliberately misaligned dummy addresses
+  const void* p = reinterpret_cast<const void*>(uintptr_t(aligned16 ? 256 : 260));
+  const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, p, p);
+  if (grid) *grid = ls.grid;
+  if (block) *block = ls.block;
+  if (groups) *groups = G;
+  return CS_OK;
+}
+
+size_t cs_workspace_bytes_for_groups(int B, int groups) {
+  if (B < 1 || groups < 1) return 0;
+  return workspace_for(B, groups);
+}
+
+size_t cs_workspace_bytes(int B, int K, int D, int similarity) {
+  const int G = cs_plan_groups(B, K, D, similarity, 1);
+  return G > 0 ? workspace_for(B, G) : 0;
+}
+
+int cs_workspace_init(void* workspace, size_t bytes, hipStream_t stream) {
+  if (workspace == nullptr) return CS_ERR_NULL_POINTER;
+  const hipError_t err = cs::launch_zero(workspace, bytes, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return CS_OK;
+}
+
+int cs_score_candidates_batch_groups(const float* queries, const float* candidates, int B,
+                                     int K, int D, int similarity, float scale,
+                                     float temperature, float* out, void* workspace,
+                                     size_t workspace_bytes, int groups, hipStream_t stream) {
+  return score(queries, candidates, B, K, D, similarity, scale, temperature, out, workspace,
+               workspace_bytes, groups, stream);
+}
+
+int cs_score_candidates_batch(const float* queries, const float* candidates, int B, int K, int D,
+                              int similarity, float scale, float temperature, float* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate(queries, candidates, out, B, K, D, similarity, scale, temperature);
+  if (st != CS_OK) return st;
+  const int G = workspace != nullptr ? plan_groups(B, K) : 1;
+  return score(queries, candidates, B, K, D, similarity, scale, temperature, out, workspace,
+               workspace_bytes, G, stream);
+}
+
+int cs_score_candidates(const float* query, const float* candidates, int K, int D,
+                        int similarity, float scale, float temperature, float* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return cs_score_candidates_batch(query, candidates, 1, K, D, similarity, scale, temperature,
+                                   out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

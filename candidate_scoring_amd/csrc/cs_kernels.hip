@@ -1,0 +1,557 @@
+// cs_kernels.hip -- gfx950 kernels for fused candidate scoring.
+//
+// Source: pull request "cuda: add a fused candidate-scoring kernel for CLM
+// and Kev". "What is fused, precisely": for cosine, a candidate's norm and
+// its dot with the query come from the same elements, so both accumulate in
+// one read of C; the softmax runs inside the workgroup with no second
+// kernel, no atomics and no global buffer for the similarities; K <= 255
+// keeps it in one workgroup's LDS; a batch is a grid over questions.
+// "Defects the GPU found", item 2: the query norm is reduced once per
+// workgroup, never once per wave and then summed again.
+//
+// Design for CDNA4 (wave64, 256 CUs in 8 XCDs):
+//  * Work item = (question b, candidate slice g). A slice is `rpg`
+//    consecutive candidates. With one slice per question this is the batch
+//    path; with several, the slices of one question run on many CUs and the
+//    last slice to finish merges their partial softmax results (below).
+//  * The query is staged once into LDS and its squared norm reduced once per
+//    workgroup. Each wave then keeps its own lanes' part of q in registers.
+//  * A wave owns R consecutive candidate rows at a time. Lane l reads
+//    16-byte pieces l, l+64, ... of every row (1 KiB per wave instruction,
+//    fully coalesced) and accumulates dot and, for cosine, the squared norm
+//    side by side from the same registers: C crosses HBM exactly once.
+//  * The R (or 2R) per-lane partial sums are reduced together with a
+//    transposed butterfly: v_permlane32_swap and v_permlane16_swap halve the
+//    set across the two 32-lane halves and the 16-lane rows, then DPP steps
+//    finish inside rows. Every candidate's sum uses the same pairing tree
+//    whatever its slot, so identical candidates give bitwise identical
+//    logits (and exactly 1/K).
+//  * Logits land in LDS only; wave 0 runs the max-subtracted softmax there
+//    and writes each probability once.
+//
+// Split merge (several slices per question): slice g writes its unnormalised
+// e_k = exp(z_k - m_g) into its own part of out and (m_g, l_g) into the
+// workspace, publishes them with an agent-scope release, and takes a ticket.
+// The slice that draws the last ticket acquires, computes M = max m_g and
+// L = sum_g l_g exp(m_g - M) over g in a fixed order (not arrival order), and
+// rescales out[k] by exp(m_g - M) / L. It then resets the ticket, so the
+// workspace is zero again and graph replays need no reset node. Nothing ever
+// waits on another workgroup.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "cs_launch.h"
+
+namespace cs {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;        // threads per workgroup (upper bound)
+constexpr int kMaxSlots = 256;     // LDS logit slots (K <= 255)
+constexpr float kNormEps2 = 1e-24f;  // (1e-12)^2: per-norm clamp of the cosine
+
+// ---------------------------------------------------------------------------
+// Cross-lane primitives (wave64).
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141; // lane <-> 7 - lane within 8 lanes
+constexpr int kDppRowRor8 = 0x128;       // lane <-> lane ^ 8 within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// Pairs lanes l and l^32 across two registers: afterwards lanes 0..31 hold
+// op(a[l], a[l+32]) and lanes 32..63 hold op(b[l-32], b[l]).
+template <class Op>
+__device__ __forceinline__ float pair32(float a, float b, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                            __builtin_bit_cast(unsigned, b), false, false);
+  return op(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Same for lanes l and l^16: rows 0 and 2 take a, rows 1 and 3 take b.
+template <class Op>
+__device__ __forceinline__ float pair16(float a, float b, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                            __builtin_bit_cast(unsigned, b), false, false);
+  return op(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// One halving step inside 16-lane rows through DPP: lanes whose BIT is clear
+// keep value i, the others value i + N/2, each combined with its partner's.
+template <int CTRL, int BIT, int N, int V, class Op>
+__device__ __forceinline__ void halve_dpp(float (&v)[V], int lane, Op op) {
+  if constexpr (N >= 2) {
+    const bool upper = (lane & BIT) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float lo = v[i], hi = v[i + N / 2];
+      const float keep = upper ? hi : lo;
+      const float send = upper ? lo : hi;
+      v[i] = op(keep, dpp_mov<CTRL>(send));
+    }
+  } else {
+    v[0] = op(v[0], dpp_mov<CTRL>(v[0]));
+  }
+}
+
+template <int N, int V, class Op>
+__device__ __forceinline__ void halve32(float (&v)[V], Op op) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] = pair32(v[i], v[i + N / 2], op);
+  } else {
+    v[0] = pair32(v[0], v[0], op);
+  }
+}
+
+template <int N, int V, class Op>
+__device__ __forceinline__ void halve16(float (&v)[V], Op op) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] = pair16(v[i], v[i + N / 2], op);
+  } else {
+    v[0] = pair16(v[0], v[0], op);
+  }
+}
+
+// Reduces V per-lane values (V a power of two, 1..64) over the 64 lanes of
+// the wave. On return every lane l holds the reduction of value index
+// l / (64 / V). Every value goes through the same lane-pairing sequence
+// (32, 16, 8, mirror-4, 2, 1), so the result for a value does not depend
+// on its index. Must be called by all 64 lanes.
+template <int V, class Op>
+__device__ __forceinline__ float wave_reduce_transposed(float (&v)[V], int lane, Op op) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+  halve32<(V >= 2 ? V : 1), V>(v, op);
+  halve16<(V >= 4 ? V / 2 : 1), V>(v, op);
+  halve_dpp<kDppRowRor8, 8, (V >= 8 ? V / 4 : 1), V>(v, lane, op);
+  halve_dpp<kDppRowHalfMirror, 4, (V >= 16 ? V / 8 : 1), V>(v, lane, op);
+  halve_dpp<kDppQuadXor2, 2, (V >= 32 ? V / 16 : 1), V>(v, lane, op);
+  halve_dpp<kDppQuadXor1, 1, (V >= 64 ? V / 32 : 1), V>(v, lane, op);
+  return v[0];
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_allreduce(float x, int lane, Op op) {
+  float v[1] = {x};
+  return wave_reduce_transposed<1>(v, lane, op);
+}
+
+// Workgroup sum in a fixed order (waves 0, 1, ...). Ends with a barrier
+// after which `scratch` may be reused.
+__device__ __forceinline__ float block_sum(float x, float* scratch, int lane, int wave,
+                                           int nwaves) {
+  x = wave_allreduce(x, lane, OpSum());
+  if (lane == 0) scratch[wave] = x;
+  __syncthreads();
+  float t = 0.0f;
+  for (int w = 0; w < nwaves; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  acc = fmaf(a.w, b.w, acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Per-workgroup state shared by the kernel variants.
+
+struct Lds {
+  float dot[kMaxSlots];
+  float ss[kMaxSlots];
+  float merge[kMaxSlots];
+  float red[kBlock / kWave];
+  int last;
+};
+
+// Writes the reduced value of slot `slot` (dot for slots < R, squared norm
+// for slots >= R) of the row group starting at candidate k0.
+template <bool COS, int R>
+__device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k0, int r0,
+                                            int r1) {
+  constexpr int V = COS ? 2 * R : R;
+  constexpr int kLanesPerSlot = kWave / V;
+  if ((lane & (kLanesPerSlot - 1)) == 0) {
+    const int slot = lane / kLanesPerSlot;
+    const int r = slot % R;
+    const int k = k0 + r;
+    if (k < r1) {
+      if (slot < R)
+        s.dot[k - r0] = total;
+      else
+        s.ss[k - r0] = total;
+    }
+  }
+}
+
+// Softmax of this slice's n logits (wave 0 only) and the store of either the
+// final probabilities (one slice per question) or the unnormalised e_k plus
+// the slice's (max, sum) partial.
+template <bool COS>
+__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, int b, int g,
+                                              int r0, int n, float zfac, int lane) {
+  float z[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = lane + kWave * i;
+    if (k < n) {
+      float v = s.dot[k];
+      if (COS) v = v * rsqrtf(fmaxf(s.ss[k], kNormEps2));
+      z[i] = v * zfac;
+      m = fmaxf(m, z[i]);
+    } else {
+      z[i] = -INFINITY;
+    }
+  }
+  m = wave_allreduce(m, lane, OpMax());
+  float e[4];
+  float l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = lane + kWave * i;
+    e[i] = (k < n) ? expf(z[i] - m) : 0.0f;
+    l += e[i];
+  }
+  l = wave_allreduce(l, lane, OpSum());
+  float* out = a.out + (size_t)b * (size_t)a.K + r0;
+  if (a.G == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = lane + kWave * i;
+      if (k < n) out[k] = e[i] / l;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = lane + kWave * i;
+      if (k < n) out[k] = e[i];
+    }
+    if (lane == 0) a.partials[(size_t)b * a.G + g] = make_float2(m, l);
+  }
+}
+
+// Called by every thread of a slice's workgroup after slice_softmax. With
+// several slices per question, the last slice to arrive merges.
+__device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, int tid,
+                                            int lane, int wave) {
+  // Publish this slice's e_k and partial at agent scope (all XCDs), then
+  // draw a ticket.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_ACQ_REL,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s.last = (t == (unsigned)(a.G - 1));
+  }
+  __syncthreads();
+  if (!s.last) return;  // uniform across the workgroup
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (wave == 0) {
+    const float2* part = a.partials + (size_t)b * a.G;
+    float mg[4];
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = lane + kWave * i;
+      mg[i] = (g < a.G) ? part[g].x : -INFINITY;
+      M = fmaxf(M, mg[i]);
+    }
+    M = wave_allreduce(M, lane, OpMax());
+    float w[4];
+    float L = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = lane + kWave * i;
+      w[i] = (g < a.G) ? expf(mg[i] - M) : 0.0f;
+      L += (g < a.G) ? part[g].y * w[i] : 0.0f;
+    }
+    L = wave_allreduce(L, lane, OpSum());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = lane + kWave * i;
+      if (g < a.G) s.merge[g] = w[i] / L;
+    }
+  }
+  __syncthreads();
+  float* out = a.out + (size_t)b * (size_t)a.K;
+  for (int k = tid; k < a.K; k += blockDim.x) out[k] = out[k] * s.merge[k / a.rpg];
+  if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Register-query kernel: D % 4 == 0, 16-byte aligned rows, D <= 256 * NV.
+// Lane l owns 16-byte pieces l + 64 j (j < NV) of q and of every row.
+
+template <bool COS, int NV, int R, bool FULL>
+__global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
+  __shared__ float4 q_lds[NV * kWave];
+  __shared__ Lds s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int D4 = a.D >> 2;
+  const long long items = (long long)a.B * a.G;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+    const int b = (int)(item / a.G), g = (int)(item % a.G);
+    const int r0 = g * a.rpg;
+    const int r1 = min(a.K, r0 + a.rpg);
+    // Stage q once; squared norm once per workgroup.
+    const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
+    float qq = 0.0f;
+    for (int i = tid; i < NV * kWave; i += blockDim.x) {
+      const float4 v = (i < D4) ? q4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      q_lds[i] = v;
+      if (COS) qq = dot4(v, v, qq);
+    }
+    float zfac = a.zscale;
+    if (COS) {
+      const float qn2 = block_sum(qq, s.red, lane, wave, nwaves);  // has barriers
+      zfac = a.zscale * rsqrtf(fmaxf(qn2, kNormEps2));
+    } else {
+      __syncthreads();
+    }
+    float4 qr[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) qr[j] = q_lds[lane + kWave * j];
+
+    const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
+    for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
+      constexpr int V = COS ? 2 * R : R;
+      float acc[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+      const float4* rows[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        rows[r] = reinterpret_cast<const float4*>(Cb + (size_t)min(k0 + r, r1 - 1) * (size_t)a.D);
+      float4 c[R][NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int idx = lane + kWave * j;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          c[r][j] = (FULL || idx < D4) ? rows[r][idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r] = dot4(c[r][j], qr[j], acc[r]);
+          if (COS) acc[R + r] = dot4(c[r][j], c[r][j], acc[R + r]);
+        }
+      }
+      const float total = wave_reduce_transposed<V>(acc, lane, OpSum());
+      store_group<COS, R>(s, total, lane, k0, r0, r1);
+    }
+    __syncthreads();
+    if (wave == 0) slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
+    if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// General kernel: any D, scalar (VEC = 1) or 16-byte (VEC = 4) pieces. The
+// query passes through LDS in chunks of at most kQChunk floats; each row's
+// partial sums of a chunk are added into its LDS slot (one wave owns a row,
+// so the additions are race-free and in chunk order).
+
+constexpr int kQChunk = 8192;
+
+template <bool COS, int VEC>
+__global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
+  extern __shared__ float q_dyn[];
+  __shared__ Lds s;
+  using VecT = typename std::conditional<VEC == 4, float4, float>::type;
+  constexpr int R = 4;
+  constexpr int V = COS ? 2 * R : R;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const long long items = (long long)a.B * a.G;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+    const int b = (int)(item / a.G), g = (int)(item % a.G);
+    const int r0 = g * a.rpg;
+    const int r1 = min(a.K, r0 + a.rpg);
+    const float* qb = a.Q + (size_t)b * (size_t)a.D;
+    const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
+    float qq = 0.0f;
+    for (int c0 = 0; c0 < a.D; c0 += kQChunk) {
+      const int clen = min(kQChunk, a.D - c0);
+      const int nv = clen / VEC;  // VEC == 4 implies D % 4 == 0
+      VecT* ql = reinterpret_cast<VecT*>(q_dyn);
+      const VecT* qs = reinterpret_cast<const VecT*>(qb + c0);
+      __syncthreads();  // the previous chunk is no longer read
+      for (int i = tid; i < nv; i += blockDim.x) {
+        const VecT v = qs[i];
+        ql[i] = v;
+        if (COS) {
+          if constexpr (VEC == 4)
+            qq = dot4(v, v, qq);
+          else
+            qq = fmaf(v, v, qq);
+        }
+      }
+      __syncthreads();
+      for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+        const VecT* rows[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          rows[r] = reinterpret_cast<const VecT*>(Cb + (size_t)min(k0 + r, r1 - 1) * (size_t)a.D +
+                                                  c0);
+        for (int i = lane; i < nv; i += kWave) {
+          const VecT qv = ql[i];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const VecT cv = rows[r][i];
+            if constexpr (VEC == 4) {
+              acc[r] = dot4(cv, qv, acc[r]);
+              if (COS) acc[R + r] = dot4(cv, cv, acc[R + r]);
+            } else {
+              acc[r] = fmaf(cv, qv, acc[r]);
+              if (COS) acc[R + r] = fmaf(cv, cv, acc[R + r]);
+            }
+          }
+        }
+        const float total = wave_reduce_transposed<V>(acc, lane, OpSum());
+        if ((lane & (kWave / V - 1)) == 0) {
+          const int slot = lane / (kWave / V);
+          const int r = slot % R;
+          const int k = k0 + r;
+          if (k < r1) {
+            float* dst = (slot < R) ? &s.dot[k - r0] : &s.ss[k - r0];
+            *dst = (c0 == 0) ? total : *dst + total;
+          }
+        }
+      }
+    }
+    float zfac = a.zscale;
+    if (COS) {
+      const float qn2 = block_sum(qq, s.red, lane, wave, nwaves);
+      zfac = a.zscale * rsqrtf(fmaxf(qn2, kNormEps2));
+    } else {
+      __syncthreads();
+    }
+    if (wave == 0) slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
+    if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
+    __syncthreads();
+  }
+}
+
+__global__ void zero_words(uint32_t* p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+__global__ void zero_bytes(uint8_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Launch selection.
+
+template <bool COS, int NV, int R>
+hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  const bool full = (a.D >> 2) == NV * kWave;
+  if (full)
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, true>), dim3(ls.grid), dim3(ls.block), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, false>), dim3(ls.grid), dim3(ls.block), 0, stream,
+                       a);
+  return hipGetLastError();
+}
+
+template <bool COS>
+hipError_t launch_regq(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  switch (ls.nv) {
+    case 1: return launch_regq_nv<COS, 1, 8>(a, ls, stream);
+    case 2: return launch_regq_nv<COS, 2, 8>(a, ls, stream);
+    case 4: return launch_regq_nv<COS, 4, 4>(a, ls, stream);
+    case 6: return launch_regq_nv<COS, 6, 2>(a, ls, stream);
+    case 8: return launch_regq_nv<COS, 8, 2>(a, ls, stream);
+    case 10: return launch_regq_nv<COS, 10, 2>(a, ls, stream);
+    case 12: return launch_regq_nv<COS, 12, 1>(a, ls, stream);
+    case 16: return launch_regq_nv<COS, 16, 1>(a, ls, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool COS>
+hipError_t launch_general(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  const size_t lds = sizeof(float) * (size_t)min(a.D, kQChunk);
+  if (ls.vec == 4)
+    hipLaunchKernelGGL((fused_general<COS, 4>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+  else
+    hipLaunchKernelGGL((fused_general<COS, 1>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int regq_rows_per_wave(int nv) {
+  switch (nv) {
+    case 1: case 2: return 8;
+    case 4: return 4;
+    case 6: case 8: case 10: return 2;
+    default: return 1;
+  }
+}
+
+int regq_nv_for(int D) {
+  const int d4 = D / 4;
+  const int need = (d4 + kWave - 1) / kWave;
+  static const int kNv[] = {1, 2, 4, 6, 8, 10, 12, 16};
+  for (int nv : kNv)
+    if (nv >= need) return nv;
+  return 0;
+}
+
+hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  if (ls.nv > 0) return a.cosine ? launch_regq<true>(a, ls, stream) : launch_regq<false>(a, ls, stream);
+  return a.cosine ? launch_general<true>(a, ls, stream) : launch_general<false>(a, ls, stream);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  uint8_t* base = static_cast<uint8_t*>(p);
+  const size_t head = std::min<size_t>((4 - (reinterpret_cast<uintptr_t>(base) & 3)) & 3, bytes);
+  if (head > 0) hipLaunchKernelGGL(zero_bytes, dim3(1), dim3(64), 0, stream, base, head);
+  const size_t words = (bytes - head) / 4;
+  if (words > 0) {
+    const size_t blocks = std::min<size_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(base + head), words);
+  }
+  const size_t tail = bytes - head - words * 4;
+  if (tail > 0)
+    hipLaunchKernelGGL(zero_bytes, dim3(1), dim3(64), 0, stream, base + head + words * 4, tail);
+  return hipGetLastError();
+}
+
+}  // namespace cs

@@ -1,0 +1,43 @@
+// cs_launch.h -- internal interface between the C ABI (cs_api.cpp) and the
+// kernels (cs_kernels.hip). Not installed, not part of the ABI.
+#ifndef CS_LAUNCH_H
+#define CS_LAUNCH_H
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+
+namespace cs {
+
+// Everything a scoring kernel reads. Pointers are device pointers.
+struct KernelArgs {
+  const float* Q;      // [B][D]
+  const float* C;      // [B][K][D]
+  float* out;          // [B][K]
+  float2* partials;    // [B][G] (max, sum) per slice; used when G > 1
+  unsigned* tickets;   // [B] arrival counters, zero at rest; used when G > 1
+  int B, K, D;
+  int G;               // slices (workgroups) per question
+  int rpg;             // candidates per slice: slice g owns [g*rpg, min(K,(g+1)*rpg))
+  float zscale;        // scale / temperature, rounded once to fp32
+  int cosine;          // 1: cosine similarity, 0: dot product
+};
+
+struct LaunchShape {
+  unsigned grid;   // workgroups (items are strided over them)
+  unsigned block;  // threads per workgroup, a multiple of 64, <= 256
+  int nv;          // > 0: register-query kernel with this many 16-byte pieces per lane
+  int vec;         // general kernel: 4 (16-byte pieces) or 1 (scalar)
+};
+
+// Rows per wave of the register-query kernel for a given nv.
+int regq_rows_per_wave(int nv);
+// Smallest instantiated nv covering D (D % 4 == 0); 0 if D is too large.
+int regq_nv_for(int D);
+
+hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace cs
+
+#endif

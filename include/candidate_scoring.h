@@ -1,0 +1,144 @@
+/*
+ * candidate_scoring.h -- C ABI of the fused candidate-scoring library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. Source: pull request "cuda: add a fused candidate-scoring
+ * kernel for CLM and Kev".
+ *   For each question b, a query q_b[D] and candidates C_b[K][D] (K <= 255)
+ *   give a probability distribution over the K candidates:
+ *       z_k = scale * s(q_b, c_bk) / temperature,
+ *       p_k = exp(z_k - max_j z_j) / sum_j exp(z_j - max_j z_j),
+ *   where s is the cosine similarity (CLM: intro table, "exp(logit_scale) *
+ *   cos(...)", so the caller passes scale = exp(logit_scale)) or the plain
+ *   dot product (Kev: intro table, scale = 1/sqrt(256)). Cosine clamps each
+ *   norm below at 1e-12, so a zero candidate scores exactly 0 and a zero
+ *   query gives the uniform distribution. The similarities never reach
+ *   global memory ("What is fused, precisely"); a batch is one launch whose
+ *   grid covers the questions.
+ *
+ * Memory and streams. Every pointer argument is a DEVICE pointer owned by
+ * the caller ("Defects the GPU found", item 1: host buffers crash the
+ * kernel rather than score wrongly). Layouts are row-major and contiguous:
+ * queries [B][D], candidates [B][K][D], out [B][K], all fp32. The library
+ * allocates nothing per call, keeps no pointer after returning, and enqueues
+ * exactly one kernel on the caller's stream without synchronizing, so a
+ * call can be captured into a hipGraph as a single node ("Verified on
+ * hardware", fourth group). Stream 0 (null stream) is allowed.
+ *
+ * Errors. Arguments are checked on the host, in a fixed order (pointers,
+ * B, K, D, similarity, scale, temperature, workspace), before any HIP call.
+ * A rejected call returns a negative status, enqueues nothing and leaves
+ * out untouched ("Verified on hardware", third group: K above 255, K of
+ * zero, D of zero, a zero scale, a negative temperature and a null query
+ * are errors). This library also rejects, as its own reading: B <= 0, null
+ * candidates or out, an unknown similarity, a NaN or infinite scale, and a
+ * zero, NaN or infinite temperature.
+ *
+ * Workspace. One-question (and small-batch) calls can spread a question's
+ * candidates over several workgroups so the whole chip works on it; the
+ * partial softmax results are merged by the last workgroup to finish. That
+ * path needs a caller-provided workspace of cs_workspace_bytes() bytes,
+ * 8-byte aligned, zeroed once with cs_workspace_init() (outside any graph
+ * capture) and left zeroed by every call. Calls that may run at the same
+ * time must not share a workspace. With workspace == NULL every question
+ * runs in one workgroup; the result is the same distribution.
+ *
+ * Thread safety: no global mutable state apart from the per-thread last HIP
+ * error; calls from several threads are safe given distinct workspaces.
+ */
+#ifndef CANDIDATE_SCORING_H
+#define CANDIDATE_SCORING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CS_ABI_VERSION 1
+/* At most 255 candidates per question ("What is fused, precisely"). */
+#define CS_MAX_K 255
+
+/* Similarity selector: CS_SIM_DOT is Kev's scaled dot product,
+ * CS_SIM_COSINE is CLM's scaled cosine ("normalize" cases, defect 2). */
+#define CS_SIM_DOT 0
+#define CS_SIM_COSINE 1
+
+/* Status codes. */
+#define CS_OK 0
+#define CS_ERR_NULL_POINTER (-1) /* query (page), candidates or out (reading) is NULL */
+#define CS_ERR_K_RANGE (-2)      /* K < 1 or K > 255 (page) */
+#define CS_ERR_D_RANGE (-3)      /* D < 1 (page) */
+#define CS_ERR_SCALE (-4)        /* scale == 0 (page), NaN or infinite (reading) */
+#define CS_ERR_TEMPERATURE (-5)  /* temperature < 0 (page), 0, NaN or infinite (reading) */
+#define CS_ERR_BATCH (-6)        /* B < 1 (reading) */
+#define CS_ERR_SIMILARITY (-7)   /* similarity is neither CS_SIM_DOT nor CS_SIM_COSINE */
+#define CS_ERR_WORKSPACE (-8)    /* workspace too small or not 8-byte aligned; bad groups */
+#define CS_ERR_LAUNCH (-9)       /* the kernel launch failed; see cs_last_hip_error() */
+#define CS_ERR_HOST_POINTER (-10) /* only with CS_DEBUG_POINTERS=1: a pointer is not device memory */
+
+/* Returns CS_ABI_VERSION. */
+int cs_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *cs_status_string(int status);
+
+/* The hipError_t of this thread's last CS_ERR_LAUNCH (0 if none). */
+int cs_last_hip_error(void);
+
+/* Workspace bytes the planned launch needs for B questions of K candidates
+ * of length D with the given similarity; 0 when that plan runs one
+ * workgroup per question and needs none. Invalid sizes return 0. */
+size_t cs_workspace_bytes(int B, int K, int D, int similarity);
+
+/* Workspace bytes for an explicit number of workgroups per question. */
+size_t cs_workspace_bytes_for_groups(int B, int groups);
+
+/* Zero `bytes` bytes of `workspace` with a kernel on `stream` (no memset
+ * node, no synchronization). Returns CS_OK, CS_ERR_NULL_POINTER or
+ * CS_ERR_LAUNCH. */
+int cs_workspace_init(void *workspace, size_t bytes, hipStream_t stream);
+
+/* Workgroups per question that cs_score_candidates_batch() would launch for
+ * these sizes, with (has_workspace != 0) or without a workspace. Both entry
+ * points use this same pure function, so a single-question call and a
+ * batch of one pick the same kernel and give bitwise the same result. */
+int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace);
+
+/* The launch cs_score_candidates_batch() would make for these sizes: grid
+ * (workgroups), block (threads) and workgroups per question, for pointers
+ * that are (aligned16 != 0) or are not 16-byte aligned. Returns CS_OK or a
+ * size-validation status. For benches that time a matching empty kernel. */
+int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
+                   unsigned *grid, unsigned *block, int *groups);
+
+/* One question: query [D], candidates [K][D], out [K] (device, fp32).
+ * Equivalent to cs_score_candidates_batch() with B = 1. */
+int cs_score_candidates(const float *query, const float *candidates, int K, int D,
+                        int similarity, float scale, float temperature, float *out,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* B independent questions in one launch: queries [B][D], candidates
+ * [B][K][D], out [B][K] (device, fp32). */
+int cs_score_candidates_batch(const float *queries, const float *candidates, int B, int K,
+                              int D, int similarity, float scale, float temperature,
+                              float *out, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* As cs_score_candidates_batch(), with the number of workgroups per
+ * question given explicitly (1 <= groups <= K; groups > 1 needs a workspace
+ * of cs_workspace_bytes_for_groups(B, groups) bytes). For tuning and tests;
+ * the distribution does not depend on groups beyond fp32 rounding. */
+int cs_score_candidates_batch_groups(const float *queries, const float *candidates, int B,
+                                     int K, int D, int similarity, float scale,
+                                     float temperature, float *out, void *workspace,
+                                     size_t workspace_bytes, int groups, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every function the header declares, arguments are rejected before
+any HIP call, planning is a pure function, and the product path is separate
+from the oracle.
+
+Rejection list source: pull request "cuda: add a fused candidate-scoring
+kernel for CLM and Kev", "Verified on hardware", third group.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import candidate_scoring_amd as cs
+from pins import STATUS_BY_NAME, rejection_cases
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "candidate_scoring.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not cs.LIBRARY.exists():
+        from candidate_scoring_amd import build
+
+        build.build()
+    return cs.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_page_entry_points():
+    names = declared_functions()
+    assert "cs_score_candidates" in names and "cs_score_candidates_batch" in names
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(cs.LIBRARY)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(cs_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_bench_library_loads(lib):
+    b = cs.load_bench()
+    for n in ("csb_time_calls", "csb_time_graph", "csb_graph_nodes", "csb_time_empty", "csb_copy"):
+        assert hasattr(b, n)
+
+
+def test_version_and_status_strings(lib):
+    assert cs.cs_abi_version() == cs.CS_ABI_VERSION == 1
+    for code in range(-10, 1):
+        s = cs.cs_status_string(code)
+        assert s and s != "unknown status", code
+    assert cs.cs_status_string(-99) == "unknown status"
+    assert cs.cs_last_hip_error() == 0
+
+
+def _host_buf(n, fill=-7.0):
+    return np.full(max(n, 1), fill, dtype=np.float32)
+
+
+CODE = {"OK": cs.CS_OK, "NULL_POINTER": cs.CS_ERR_NULL_POINTER, "K_RANGE": cs.CS_ERR_K_RANGE,
+        "D_RANGE": cs.CS_ERR_D_RANGE, "SCALE": cs.CS_ERR_SCALE,
+        "TEMPERATURE": cs.CS_ERR_TEMPERATURE, "BATCH": cs.CS_ERR_BATCH,
+        "SIMILARITY": cs.CS_ERR_SIMILARITY}
+
+
+def test_status_codes_match_the_oracle_numbering():
+    # same published list, numbered independently on each side
+    assert CODE == STATUS_BY_NAME
+
+
+@pytest.mark.parametrize("case", rejection_cases(), ids=lambda c: f"{c[0]}:{list(c[1].items())[0]}")
+def test_rejected_before_any_device_work(lib, case):
+    """Each rejected argument returns its code; the host buffers passed as
+    pointers are never touched (the call returns before any HIP call)."""
+    origin, change, expect = case
+    q, c, out = _host_buf(8), _host_buf(32), _host_buf(64)
+    args = dict(query=q.ctypes.data, candidates=c.ctypes.data, out=out.ctypes.data, B=1, K=4,
+                D=8, similarity=0, scale=1.0, temperature=1.0)
+    for k, v in change.items():
+        args[k] = None if v is None else v
+        if k in ("query", "candidates", "out") and v is None:
+            args[k] = None
+    st = lib.cs_score_candidates_batch(args["query"], args["candidates"], args["B"], args["K"],
+                                       args["D"], args["similarity"], args["scale"],
+                                       args["temperature"], args["out"], None, 0, None)
+    assert st == CODE[expect], (origin, change, st)
+    assert np.all(out == -7.0) and np.all(q == -7.0) and np.all(c == -7.0)
+    if "B" not in change:
+        st1 = lib.cs_score_candidates(args["query"], args["candidates"], args["K"], args["D"],
+                                      args["similarity"], args["scale"], args["temperature"],
+                                      args["out"], None, 0, None)
+        assert st1 == CODE[expect]
+
+
+def test_workspace_and_group_rejections(lib):
+    q, c, out = _host_buf(512), _host_buf(255 * 512), _host_buf(255)
+    ws = np.zeros(1 << 16, dtype=np.uint8)
+    base = (q.ctypes.data, c.ctypes.data, 1, 255, 512, 1, 14.285714, 1.0, out.ctypes.data)
+    # split path without a workspace
+    assert lib.cs_score_candidates_batch_groups(*base, None, 0, 4, None) == cs.CS_ERR_WORKSPACE
+    # too small
+    need = cs.cs_workspace_bytes_for_groups(1, 4)
+    assert need > 0
+    assert lib.cs_score_candidates_batch_groups(*base, ws.ctypes.data, need - 1, 4,
+                                                None) == cs.CS_ERR_WORKSPACE
+    # misaligned
+    assert lib.cs_score_candidates_batch_groups(*base, ws.ctypes.data + 4, need + 64, 4,
+                                                None) == cs.CS_ERR_WORKSPACE
+    # group counts outside 1..K, or leaving an empty slice (K=255, 254 groups)
+    for g in (0, -1, 256, 254):
+        assert lib.cs_score_candidates_batch_groups(*base, ws.ctypes.data, ws.size, g,
+                                                    None) == cs.CS_ERR_WORKSPACE
+    # the argument checks come first
+    bad_k = (q.ctypes.data, c.ctypes.data, 1, 256, 512, 1, 1.0, 1.0, out.ctypes.data)
+    assert lib.cs_score_candidates_batch_groups(*bad_k, None, 0, 4, None) == cs.CS_ERR_K_RANGE
+    assert np.all(out == -7.0)
+    assert lib.cs_workspace_init(None, 64, None) == cs.CS_ERR_NULL_POINTER
+
+
+def test_planning_is_pure_and_shared(lib):
+    # no workspace: one workgroup per question
+    for B, K, D in ((1, 5, 512), (1, 255, 512), (8, 255, 512), (1024, 255, 2560)):
+        assert cs.cs_plan_groups(B, K, D, 1, False) == 1
+    # with a workspace: a small batch spreads over the chip, a big one does not
+    assert cs.cs_plan_groups(1, 255, 512, 1, True) > 1
+    assert cs.cs_plan_groups(8, 255, 512, 1, True) > 1
+    assert cs.cs_plan_groups(1024, 255, 2560, 0, True) == 1
+    assert cs.cs_plan_groups(1, 1, 512, 1, True) == 1
+    for B, K in ((1, 255), (3, 17), (8, 255), (100, 64)):
+        G = cs.cs_plan_groups(B, K, 64, 0, True)
+        rpg = -(-K // G)
+        assert -(-K // rpg) == G, "planned slices must all be nonempty"
+        assert cs.cs_workspace_bytes(B, K, 64, 0) == (
+            cs.cs_workspace_bytes_for_groups(B, G) if G > 1 else 0)
+    # invalid sizes plan nothing
+    assert cs.cs_plan_groups(0, 5, 5, 0, True) == 0
+    assert cs.cs_plan_groups(1, 256, 5, 0, True) == 0
+    assert cs.cs_workspace_bytes(1, 0, 5, 0) == 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        cs._ptr(t)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """Neither the package nor its native code imports, links or names the
+    oracle; the oracle in turn does not import the package."""
+    pkg = ROOT / "candidate_scoring_amd"
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.cpp")) + \
+            list(pkg.rglob("*.h")):
+        text = f.read_text()
+        assert "import oracle" not in text and "from oracle" not in text, f
+        assert "cs_oracle" not in text and "cso_" not in text, f
+    for f in (ROOT / "oracle").glob("*"):
+        if f.suffix in (".py", ".c", ".h"):
+            text = f.read_text()
+            assert "candidate_scoring_amd" not in text and "candidate_scoring.h" not in text, f
+    if cs.LIBRARY.exists():
+        out = subprocess.run(["nm", "-D", str(cs.LIBRARY)], capture_output=True, text=True).stdout
+        assert "cso_" not in out
+        deps = subprocess.run(["ldd", str(cs.LIBRARY)], capture_output=True, text=True).stdout
+        assert "oracle" not in deps
