@@ -82,17 +82,23 @@ struct OpMax {
 // op(a[l], a[l+32]) and lanes 32..63 hold op(b[l-32], b[l]).
 template <class Op>
 __device__ __forceinline__ float pair32(float a, float b, Op op) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                            __builtin_bit_cast(unsigned, b), false, false);
-  return op(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  // Copy the two results out before reinterpreting them: bit-casting a
+  // vector element in place reads element 0 for both.
+  const unsigned r0 = r[0], r1 = r[1];
+  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // Same for lanes l and l^16: rows 0 and 2 take a, rows 1 and 3 take b.
 template <class Op>
 __device__ __forceinline__ float pair16(float a, float b, Op op) {
-  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
-                                            __builtin_bit_cast(unsigned, b), false, false);
-  return op(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  // Copy the two results out before reinterpreting them: bit-casting a
+  // vector element in place reads element 0 for both.
+  const unsigned r0 = r[0], r1 = r[1];
+  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // One halving step inside 16-lane rows through DPP: lanes whose BIT is clear
