@@ -263,7 +263,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "fused_regq<dot, nv=10, rows=2, full>",
+                     "kernel": "fused_regq<dot, nv=10, rows=2, full, nontemporal>",
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
     }
     if not args.no_latency:

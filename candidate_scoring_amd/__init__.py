@@ -108,6 +108,7 @@ def load_bench(path: Path | str = BENCH_LIBRARY):
         "csb_graph_replay": [cp, i32, i32],
         "csb_time_empty": [u32, u32, i32, i32, i32, vp, f32p],
         "csb_copy": [vp, vp, ctypes.c_size_t, vp],
+        "csb_read": [vp, ctypes.c_size_t, u32, u32, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)

@@ -17,6 +17,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "cs_launch.h"
 
@@ -25,11 +26,22 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 4;
-// Workgroups a small batch is spread over: two per CU on a 256-CU MI355X.
-constexpr int kSplitTarget = 512;
-// Questions at or above which a batch already fills the chip on its own.
-constexpr int kSplitMaxB = 256;
+constexpr int kMaxWaves = 8;       // one workgroup per question: up to 512 threads
+constexpr int kMaxSplitWaves = 4;  // a slice of a split question: up to 256 threads
+// Slicing model. Spreading a question over G workgroups divides its
+// streaming time by G but costs every slice an agent-scope release (an L2
+// write-back, which the chip serialises at roughly 20 ns each) plus a merge.
+// With a workgroup streaming about 120 GB/s, the time
+//   bytes_q / (G * 120 GB/s) + B * G * 20 ns
+// is smallest at G* = sqrt(bytes_q / (B * 2400 B)). Splitting pays only when
+// G* is large enough to beat one fuller workgroup per question; measured on
+// MI355X for K = 255, D = 512 and 2560, B = 1 .. 1024, that is G* >= 5.
+constexpr double kSliceBalanceBytes = 2400.0;
+// Candidate blocks larger than all eight XCD L2 caches together are streamed
+// with non-temporal loads.
+constexpr double kStreamBytes = 32.0 * 1024 * 1024;
+constexpr double kMinUsefulSlices = 5.0;
+constexpr int kMaxSlices = 64;
 // Grid cap; items beyond it are strided over the resident workgroups.
 constexpr long long kGridCap = 1 << 20;
 
@@ -72,9 +84,12 @@ bool is_device_pointer(const void* p) {
   return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
 }
 
-int plan_groups(int B, int K) {
-  if (B >= kSplitMaxB || K == 1) return 1;
-  int G = std::min(K, (kSplitTarget + B - 1) / B);
+int plan_groups(int B, int K, int D) {
+  if (K == 1) return 1;
+  const double bytes_q = 4.0 * (double)K * (double)D;
+  const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
+  if (g_star < kMinUsefulSlices) return 1;
+  const int G = std::min({K, kMaxSlices, (int)std::lround(g_star)});
   const int rpg = (K + G - 1) / G;
   return (K + rpg - 1) / rpg;  // no empty slices
 }
@@ -82,15 +97,16 @@ int plan_groups(int B, int K) {
 // Launch shape for a validated call: kernel variant from D and alignment,
 // up to four waves per workgroup (enough for the slice's rows).
 cs::LaunchShape make_shape(int B, int K, int D, int G, int rpg, const void* Q, const void* C) {
-  (void)K;
   cs::LaunchShape ls;
   const bool aligned16 = (reinterpret_cast<uintptr_t>(Q) & 15u) == 0 &&
                          (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
   const bool vec4 = (D % 4 == 0) && aligned16;
   ls.nv = vec4 ? cs::regq_nv_for(D) : 0;
   ls.vec = vec4 ? 4 : 1;
+  ls.nt = 4.0 * (double)B * (double)K * (double)D >= kStreamBytes ? 1 : 0;
   const int rows_per_wave = ls.nv > 0 ? cs::regq_rows_per_wave(ls.nv) : 4;
-  const int waves = std::max(1, std::min(kMaxWaves, (rpg + rows_per_wave - 1) / rows_per_wave));
+  const int max_waves = G > 1 ? kMaxSplitWaves : kMaxWaves;
+  const int waves = std::max(1, std::min(max_waves, (rpg + rows_per_wave - 1) / rows_per_wave));
   ls.block = (unsigned)(waves * kWave);
   ls.grid = (unsigned)std::min<long long>((long long)B * G, kGridCap);
   return ls;
@@ -168,7 +184,7 @@ int cs_last_hip_error(void) { return g_last_hip_error; }
 
 int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace) {
   if (validate(&B, &B, &B, B, K, D, similarity, 1.0f, 1.0f) != CS_OK) return 0;
-  return has_workspace ? plan_groups(B, K) : 1;
+  return has_workspace ? plan_groups(B, K, D) : 1;
 }
 
 int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
@@ -218,7 +234,7 @@ int cs_score_candidates_batch(const float* queries, const float* candidates, int
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = validate(queries, candidates, out, B, K, D, similarity, scale, temperature);
   if (st != CS_OK) return st;
-  const int G = workspace != nullptr ? plan_groups(B, K) : 1;
+  const int G = workspace != nullptr ? plan_groups(B, K, D) : 1;
   return score(queries, candidates, B, K, D, similarity, scale, temperature, out, workspace,
                workspace_bytes, G, stream);
 }

@@ -14,6 +14,8 @@
 //   csb_time_empty   the same protocol for an empty kernel of a given
 //                    grid/block: the launch floor
 //   csb_copy         plain device copy of `bytes` (counter calibration)
+//   csb_read         plain streaming read of `bytes` (the practical HBM read
+//                    ceiling that the scoring kernel is compared with)
 
 #include <hip/hip_runtime.h>
 
@@ -45,6 +47,20 @@ __global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
     dst[i] = src[i];
+}
+
+// Streams n 16-byte pieces, four in flight per thread; the sum only keeps
+// the loads alive and is stored only if it hits an impossible value.
+__global__ void read_kernel(const float4* __restrict__ src, size_t n, float* sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float acc = 0.0f;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const float4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc += (a.x + b.x) + (c.x + d.x) + (a.w + b.w) + (c.w + d.w);
+  }
+  for (; i < n; i += stride) acc += src[i].x;
+  if (acc == -1.2345e-30f) sink[0] = acc;
 }
 
 int hip_code(hipError_t e) { return e == hipSuccess ? 0 : -1000 - (int)e; }
@@ -176,6 +192,15 @@ int csb_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   const size_t n = bytes / 16;
   hipLaunchKernelGGL(copy_kernel, dim3(4096), dim3(256), 0, stream,
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  return hip_code(hipGetLastError());
+}
+
+int csb_read(const void* src, size_t bytes, unsigned grid, unsigned block, float* sink,
+             hipStream_t stream) {
+  if (src == nullptr || sink == nullptr || (bytes % 16) != 0 || block == 0 || block > 1024)
+    return -1;
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(block), 0, stream,
+                     static_cast<const float4*>(src), bytes / 16, sink);
   return hip_code(hipGetLastError());
 }
 

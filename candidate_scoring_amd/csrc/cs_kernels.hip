@@ -52,7 +52,7 @@ namespace cs {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;        // threads per workgroup (upper bound)
+constexpr int kBlock = 512;        // threads per workgroup (upper bound)
 constexpr int kMaxSlots = 256;     // LDS logit slots (K <= 255)
 constexpr float kNormEps2 = 1e-24f;  // (1e-12)^2: per-norm clamp of the cosine
 
@@ -69,6 +69,30 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Candidate rows are read exactly once; when the block of candidates is far
+// larger than the L2 caches, loading them non-temporally keeps them from
+// evicting anything useful (the streaming read then runs at the same rate as
+// a plain read-only copy kernel).
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float4* p) {
+  if constexpr (NT) {
+    const v4f_t v = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ float load1(const float* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
 }
 
 struct OpSum {
@@ -265,26 +289,39 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
 // several slices per question, the last slice to arrive merges.
 __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, int tid,
                                             int lane, int wave) {
-  // Publish this slice's e_k and partial at agent scope (all XCDs), then
-  // draw a ticket.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_ACQ_REL,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    s.last = (t == (unsigned)(a.G - 1));
+  // Only wave 0 wrote global memory (e_k and the partial). It publishes them
+  // at agent scope (all XCDs: L2 write-back) and draws the ticket; the
+  // release fence orders the stores before the relaxed ticket increment.
+  if (wave == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) {
+      const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      s.last = (t == (unsigned)(a.G - 1));
+    }
   }
   __syncthreads();
   if (!s.last) return;  // uniform across the workgroup
+  // Last slice: acquire the other slices' stores (L2 invalidate), fetch the
+  // e_k to rescale while wave 0 reads the partials.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  float* out = a.out + (size_t)b * (size_t)a.K;
+  float ek[kMaxSlots / kWave];
+#pragma unroll
+  for (int i = 0; i < kMaxSlots / kWave; ++i) {
+    const int k = tid + (int)blockDim.x * i;
+    ek[i] = (k < a.K) ? out[k] : 0.0f;
+  }
   if (wave == 0) {
     const float2* part = a.partials + (size_t)b * a.G;
-    float mg[4];
+    float mg[4], lg[4];
     float M = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = lane + kWave * i;
-      mg[i] = (g < a.G) ? part[g].x : -INFINITY;
+      const float2 v = (g < a.G) ? part[g] : make_float2(-INFINITY, 0.0f);
+      mg[i] = v.x;
+      lg[i] = v.y;
       M = fmaxf(M, mg[i]);
     }
     M = wave_allreduce(M, lane, OpMax());
@@ -294,7 +331,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, 
     for (int i = 0; i < 4; ++i) {
       const int g = lane + kWave * i;
       w[i] = (g < a.G) ? expf(mg[i] - M) : 0.0f;
-      L += (g < a.G) ? part[g].y * w[i] : 0.0f;
+      L += lg[i] * w[i];
     }
     L = wave_allreduce(L, lane, OpSum());
 #pragma unroll
@@ -304,18 +341,24 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, 
     }
   }
   __syncthreads();
-  float* out = a.out + (size_t)b * (size_t)a.K;
-  for (int k = tid; k < a.K; k += blockDim.x) out[k] = out[k] * s.merge[k / a.rpg];
+#pragma unroll
+  for (int i = 0; i < kMaxSlots / kWave; ++i) {
+    const int k = tid + (int)blockDim.x * i;
+    if (k < a.K) out[k] = ek[i] * s.merge[k / a.rpg];
+  }
   if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
 // Register-query kernel: D % 4 == 0, 16-byte aligned rows, D <= 256 * NV.
-// Lane l owns 16-byte pieces l + 64 j (j < NV) of q and of every row.
+// Lane l owns 16-byte pieces l + 64 j (j < NV) of q and of every row. Each
+// wave loads its pieces of q straight into registers, in the same burst as
+// its first candidate rows, so no separate staging round trip precedes the
+// hot loop; the query's squared norm is reduced once per workgroup (by wave
+// 0, which holds all of q) right before the softmax.
 
-template <bool COS, int NV, int R, bool FULL>
+template <bool COS, int NV, int R, bool FULL, bool NT>
 __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
-  __shared__ float4 q_lds[NV * kWave];
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
@@ -325,24 +368,13 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
     const int b = (int)(item / a.G), g = (int)(item % a.G);
     const int r0 = g * a.rpg;
     const int r1 = min(a.K, r0 + a.rpg);
-    // Stage q once; squared norm once per workgroup.
     const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
-    float qq = 0.0f;
-    for (int i = tid; i < NV * kWave; i += blockDim.x) {
-      const float4 v = (i < D4) ? q4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      q_lds[i] = v;
-      if (COS) qq = dot4(v, v, qq);
-    }
-    float zfac = a.zscale;
-    if (COS) {
-      const float qn2 = block_sum(qq, s.red, lane, wave, nwaves);  // has barriers
-      zfac = a.zscale * rsqrtf(fmaxf(qn2, kNormEps2));
-    } else {
-      __syncthreads();
-    }
     float4 qr[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) qr[j] = q_lds[lane + kWave * j];
+    for (int j = 0; j < NV; ++j) {
+      const int idx = lane + kWave * j;
+      qr[j] = (FULL || idx < D4) ? q4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
     for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
@@ -360,7 +392,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         const int idx = lane + kWave * j;
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          c[r][j] = (FULL || idx < D4) ? rows[r][idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+          c[r][j] = (FULL || idx < D4) ? load4<NT>(rows[r] + idx) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
@@ -374,7 +406,17 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
       store_group<COS, R>(s, total, lane, k0, r0, r1);
     }
     __syncthreads();
-    if (wave == 0) slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
+    if (wave == 0) {
+      float zfac = a.zscale;
+      if (COS) {
+        float qq = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) qq = dot4(qr[j], qr[j], qq);
+        qq = wave_allreduce(qq, lane, OpSum());
+        zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
+      }
+      slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
+    }
     if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
     __syncthreads();
   }
@@ -388,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
 
 constexpr int kQChunk = 8192;
 
-template <bool COS, int VEC>
+template <bool COS, int VEC, bool NT>
 __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   extern __shared__ float q_dyn[];
   __shared__ Lds s;
@@ -435,7 +477,11 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
           const VecT qv = ql[i];
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const VecT cv = rows[r][i];
+            VecT cv;
+            if constexpr (VEC == 4)
+              cv = load4<NT>(rows[r] + i);
+            else
+              cv = load1<NT>(rows[r] + i);
             if constexpr (VEC == 4) {
               acc[r] = dot4(cv, qv, acc[r]);
               if (COS) acc[R + r] = dot4(cv, cv, acc[R + r]);
@@ -483,40 +529,48 @@ __global__ void zero_bytes(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Launch selection.
 
-template <bool COS, int NV, int R>
+template <bool COS, int NV, int R, bool NT>
 hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const bool full = (a.D >> 2) == NV * kWave;
   if (full)
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, true>), dim3(ls.grid), dim3(ls.block), 0, stream, a);
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT>), dim3(ls.grid), dim3(ls.block), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, false>), dim3(ls.grid), dim3(ls.block), 0, stream,
-                       a);
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT>), dim3(ls.grid), dim3(ls.block), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <bool COS>
+template <bool COS, bool NT>
 hipError_t launch_regq(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   switch (ls.nv) {
-    case 1: return launch_regq_nv<COS, 1, 8>(a, ls, stream);
-    case 2: return launch_regq_nv<COS, 2, 8>(a, ls, stream);
-    case 4: return launch_regq_nv<COS, 4, 4>(a, ls, stream);
-    case 6: return launch_regq_nv<COS, 6, 2>(a, ls, stream);
-    case 8: return launch_regq_nv<COS, 8, 2>(a, ls, stream);
-    case 10: return launch_regq_nv<COS, 10, 2>(a, ls, stream);
-    case 12: return launch_regq_nv<COS, 12, 1>(a, ls, stream);
-    case 16: return launch_regq_nv<COS, 16, 1>(a, ls, stream);
+    case 1: return launch_regq_nv<COS, 1, 8, NT>(a, ls, stream);
+    case 2: return launch_regq_nv<COS, 2, 8, NT>(a, ls, stream);
+    case 4: return launch_regq_nv<COS, 4, 4, NT>(a, ls, stream);
+    case 6: return launch_regq_nv<COS, 6, 2, NT>(a, ls, stream);
+    case 8: return launch_regq_nv<COS, 8, 2, NT>(a, ls, stream);
+    case 10: return launch_regq_nv<COS, 10, 2, NT>(a, ls, stream);
+    case 12: return launch_regq_nv<COS, 12, 1, NT>(a, ls, stream);
+    case 16: return launch_regq_nv<COS, 16, 1, NT>(a, ls, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool COS>
+template <bool COS, bool NT>
 hipError_t launch_general(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const size_t lds = sizeof(float) * (size_t)min(a.D, kQChunk);
   if (ls.vec == 4)
-    hipLaunchKernelGGL((fused_general<COS, 4>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+    hipLaunchKernelGGL((fused_general<COS, 4, NT>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
   else
-    hipLaunchKernelGGL((fused_general<COS, 1>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+    hipLaunchKernelGGL((fused_general<COS, 1, NT>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
   return hipGetLastError();
+}
+
+template <bool COS>
+hipError_t launch_cos(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  if (ls.nv > 0)
+    return ls.nt ? launch_regq<COS, true>(a, ls, stream) : launch_regq<COS, false>(a, ls, stream);
+  return ls.nt ? launch_general<COS, true>(a, ls, stream) : launch_general<COS, false>(a, ls, stream);
 }
 
 }  // namespace
@@ -540,8 +594,7 @@ int regq_nv_for(int D) {
 }
 
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
-  if (ls.nv > 0) return a.cosine ? launch_regq<true>(a, ls, stream) : launch_regq<false>(a, ls, stream);
-  return a.cosine ? launch_general<true>(a, ls, stream) : launch_general<false>(a, ls, stream);
+  return a.cosine ? launch_cos<true>(a, ls, stream) : launch_cos<false>(a, ls, stream);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {

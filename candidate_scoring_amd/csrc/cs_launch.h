@@ -28,6 +28,7 @@ struct LaunchShape {
   unsigned block;  // threads per workgroup, a multiple of 64, <= 256
   int nv;          // > 0: register-query kernel with this many 16-byte pieces per lane
   int vec;         // general kernel: 4 (16-byte pieces) or 1 (scalar)
+  int nt;          // 1: load candidates non-temporally (streamed, larger than L2)
 };
 
 // Rows per wave of the register-query kernel for a given nv.

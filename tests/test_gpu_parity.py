@@ -286,3 +286,28 @@ def test_headline_batch_full_size(cs, orc, dev):
     out = cs.score(q, c, w.similarity, float(w.scale), float(w.temperature))
     torch.cuda.synchronize()
     check(out.cpu().numpy(), want, "headline batch")
+
+
+@pytest.mark.parametrize("B,K,D,sim,offset", [(64, 255, 2560, "dot", 0), (40, 255, 1024, "cosine", 0),
+                                              (24, 200, 2049, "cosine", 0), (16, 255, 2560, "dot", 1)])
+def test_streaming_paths(cs, orc, dev, B, K, D, sim, offset):
+    """Candidate blocks above 32 MiB take the non-temporal streaming
+    variants (register-query and general kernels), with and without a
+    workspace."""
+    import torch
+
+    assert 4 * B * K * D >= 32 * 1024 * 1024
+    Q, C = workloads.normal_inputs(29, B, K, D)
+    scale = 14.285714 if sim == "cosine" else 0.0625
+    want = orc.score(Q, C, sim, scale)
+    qd = torch.zeros(B * D + offset, dtype=torch.float32, device=dev)
+    cd = torch.zeros(B * K * D + offset, dtype=torch.float32, device=dev)
+    qd[offset:] = to_dev(Q.reshape(-1), dev)
+    cd[offset:] = to_dev(C.reshape(-1), dev)
+    q, c = qd[offset:].view(B, D), cd[offset:].view(B, K, D)
+    for ws in (False, True):
+        note(f"case streaming B={B} K={K} D={D} {sim} offset={offset} ws={ws} "
+             f"groups={cs.cs_plan_groups(B, K, D, sim, ws)}")
+        out = cs.score(q, c, sim, scale, 1.0, use_workspace=ws)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), want, f"streaming B={B} D={D} ws={ws}")
