@@ -14,12 +14,15 @@
 //    consecutive candidates. With one slice per question this is the batch
 //    path; with several, the slices of one question run on many CUs and the
 //    last slice to finish merges their partial softmax results (below).
-//  * The query is staged once into LDS and its squared norm reduced once per
-//    workgroup. Each wave then keeps its own lanes' part of q in registers.
 //  * A wave owns R consecutive candidate rows at a time. Lane l reads
 //    16-byte pieces l, l+64, ... of every row (1 KiB per wave instruction,
 //    fully coalesced) and accumulates dot and, for cosine, the squared norm
 //    side by side from the same registers: C crosses HBM exactly once.
+//    Large candidate blocks are loaded non-temporally (streamed).
+//  * For D <= 4096 each wave holds its pieces of q in registers, loaded in
+//    the same burst as its first rows; wave 0 reduces |q|^2 once per
+//    workgroup. Larger or unaligned D use the general kernel, which stages q
+//    through LDS in chunks and reduces |q|^2 once per workgroup there.
 //  * The R (or 2R) per-lane partial sums are reduced together with a
 //    transposed butterfly: v_permlane32_swap and v_permlane16_swap halve the
 //    set across the two 32-lane halves and the 16-lane rows, then DPP steps
