@@ -114,6 +114,15 @@ class Device:
             raise RuntimeError(f"csb_time_calls failed: {st}")
         return ms.value
 
+    def time_rotating(self, call, copies, q_stride, c_stride, out_stride, iters) -> float:
+        ms = ctypes.c_float()
+        st = self.bench.csb_time_calls_rotating(ctypes.byref(call), copies, q_stride, c_stride,
+                                                out_stride, iters, self.stream.cuda_stream,
+                                                ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"csb_time_calls_rotating failed: {st}")
+        return ms.value
+
     def time_graph(self, call, replays, warmup=20):
         ms, nodes = ctypes.c_float(), ctypes.c_size_t()
         st = self.bench.csb_time_graph(ctypes.byref(call), 1, replays, warmup, ctypes.byref(ms),
@@ -153,6 +162,63 @@ def latency_section(devc, replays):
                           "empty_kernel_graph_floor_us": round(1e3 * f_ms / replays, 3)}
         res[name] = row
         log(f"latency {name}: {row}")
+        del q, c, out
+    return res
+
+
+def ab_section(devc, iters, headline=None):
+    """Fused vs the unfused baseline (separate norm pass + scoring that loads
+    the staged norms) on the page's results-table shapes and the Kev batch.
+    Direct back-to-back calls, warm caches for the small shapes."""
+    torch = devc.torch
+    res = {}
+    for name in workloads.AB_SHAPES:
+        if name == workloads.HEADLINE and headline is not None:
+            w, q, c, out = headline
+        else:
+            w = workloads.make(name)
+            q, c, out = devc.upload(w)
+        norms = torch.empty(w.B * w.K, dtype=torch.float32, device=devc.dev)
+        planned, _ws = devc.call(w, q, c, out, use_workspace=True)
+        one_wg, _ = devc.call(w, q, c, out, use_workspace=False)
+        unfused, _ = devc.call(w, q, c, out, use_workspace=False)
+        unfused.row_norms = norms.data_ptr()
+        n = iters if w.B * w.K * w.D < 50_000_000 else 10
+        t = {}
+        for label, call in (("fused", planned), ("fused_one_wg_per_question", one_wg),
+                            ("unfused", unfused)):
+            devc.time_calls(call, 3)
+            t[label] = 1e3 * devc.time_calls(call, n) / n
+        res[name] = {"B": w.B, "K": w.K, "D": w.D, "similarity": w.similarity,
+                     "fused_us": round(t["fused"], 3),
+                     "fused_one_wg_per_question_us": round(t["fused_one_wg_per_question"], 3),
+                     "unfused_us": round(t["unfused"], 3),
+                     "unfused_over_fused": round(t["unfused"] / t["fused"], 3),
+                     "unfused_over_fused_one_wg": round(t["unfused"] / t["fused_one_wg_per_question"], 3)}
+        log(f"a/b {name}: {res[name]}")
+        if not (name == workloads.HEADLINE and headline is not None):
+            del q, c, out
+    return res
+
+
+def cold_section(devc, iters, target_bytes=768 << 20):
+    """Single-question and small-batch calls with cold caches: each call
+    reads the next of enough input copies to exceed the 256 MB Infinity
+    Cache and the L2s several times over (direct calls, planned split)."""
+    torch = devc.torch
+    res = {}
+    for name in LATENCY_CONFIGS:
+        w = workloads.make(name)
+        per = w.B * w.K * w.D * 4
+        copies = max(2, -(-target_bytes // per))
+        q = torch.from_numpy(w.Q).to(devc.dev).reshape(-1).repeat(copies)
+        c = torch.from_numpy(w.C).to(devc.dev).reshape(-1).repeat(copies)
+        out = torch.empty(copies * w.B * w.K, dtype=torch.float32, device=devc.dev)
+        call, _ws = devc.call(w, q, c, out, use_workspace=True)
+        devc.time_rotating(call, copies, w.B * w.D, w.B * w.K * w.D, w.B * w.K, copies)
+        ms = devc.time_rotating(call, copies, w.B * w.D, w.B * w.K * w.D, w.B * w.K, iters)
+        res[name] = {"copies": copies, "cold_direct_us_per_call": round(1e3 * ms / iters, 3)}
+        log(f"cold {name}: {res[name]}")
         del q, c, out
     return res
 
@@ -197,6 +263,7 @@ def main():
     ap.add_argument("--replays", type=int, default=2000, help="graph replays per latency figure")
     ap.add_argument("--no-latency", action="store_true", help="skip the small-shape latencies")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-ab", action="store_true", help="skip the fused vs unfused table")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -245,6 +312,8 @@ def main():
         err = float(np.max(np.abs(got[b].astype(np.float64) - want)))
         if not err <= 1e-4:
             raise SystemExit(f"parity failure on question {b}: {err}")
+
+    ab = None if args.no_ab else ab_section(devc, 2000, headline=(w, q, c, out))
     del q, c, out
 
     traffic = committed_traffic()
@@ -274,6 +343,9 @@ def main():
     }
     if not args.no_latency:
         result["latency"] = latency_section(devc, args.replays)
+        result["cold_latency"] = cold_section(devc, 2000)
+    if ab is not None:
+        result["fused_vs_unfused"] = ab
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -72,6 +72,7 @@ def load(path: Path | str = LIBRARY):
         "cs_score_candidates_batch": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
         "cs_score_candidates_batch_groups": (
             i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, i32, vp]),
+        "cs_score_candidates_unfused": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -85,7 +86,8 @@ class CsbCall(ctypes.Structure):
                 ("B", ctypes.c_int), ("K", ctypes.c_int), ("D", ctypes.c_int),
                 ("similarity", ctypes.c_int), ("scale", ctypes.c_float),
                 ("temperature", ctypes.c_float), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("groups", ctypes.c_int)]
+                ("workspace_bytes", ctypes.c_size_t), ("groups", ctypes.c_int),
+                ("row_norms", ctypes.c_void_p)]
 
 
 def load_bench(path: Path | str = BENCH_LIBRARY):
@@ -103,6 +105,8 @@ def load_bench(path: Path | str = BENCH_LIBRARY):
     cp = ctypes.POINTER(CsbCall)
     sigs = {
         "csb_time_calls": [cp, i32, vp, f32p],
+        "csb_time_calls_rotating": [cp, i32, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_size_t,
+                                    i32, vp, f32p],
         "csb_graph_nodes": [cp, szp],
         "csb_time_graph": [cp, i32, i32, i32, f32p, szp],
         "csb_graph_replay": [cp, i32, i32],
@@ -209,6 +213,14 @@ def cs_score_candidates_batch_groups(queries, candidates, B: int, K: int, D: int
     return load().cs_score_candidates_batch_groups(
         _ptr(queries), _ptr(candidates), B, K, D, _sim(similarity), scale, temperature,
         _ptr(out), _ptr(workspace), workspace_bytes, groups, _stream(stream))
+
+
+def cs_score_candidates_unfused(queries, candidates, B: int, K: int, D: int, similarity,
+                                scale: float, temperature: float, out, row_norms,
+                                stream=None) -> int:
+    return load().cs_score_candidates_unfused(_ptr(queries), _ptr(candidates), B, K, D,
+                                              _sim(similarity), scale, temperature, _ptr(out),
+                                              _ptr(row_norms), _stream(stream))
 
 
 # ----------------------------------------------------------------------------

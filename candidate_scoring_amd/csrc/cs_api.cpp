@@ -147,9 +147,46 @@ int score(const float* Q, const float* C, int B, int K, int D, int sim, float sc
   // scale / T rounded once to fp32 from the exact double quotient.
   a.zscale = (float)((double)scale / (double)temperature);
   a.cosine = sim == CS_SIM_COSINE;
+  a.staged_norms = nullptr;
 
   const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, Q, C);
   const hipError_t err = cs::launch_fused(a, ls, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return CS_OK;
+}
+
+// Unfused baseline: a norm pass stages |c_k| in `norms`, then the scoring
+// kernel (one workgroup per question) loads it instead of accumulating it.
+int score_unfused(const float* Q, const float* C, int B, int K, int D, int sim, float scale,
+                  float temperature, float* out, float* norms, hipStream_t stream) {
+  int st = validate(Q, C, out, B, K, D, sim, scale, temperature);
+  if (st != CS_OK) return st;
+  if (norms == nullptr || (reinterpret_cast<uintptr_t>(norms) & 3u) != 0) return CS_ERR_WORKSPACE;
+  if (debug_pointers()) {
+    if (!is_device_pointer(Q) || !is_device_pointer(C) || !is_device_pointer(out) ||
+        !is_device_pointer(norms))
+      return CS_ERR_HOST_POINTER;
+  }
+  cs::KernelArgs a;
+  a.Q = Q;
+  a.C = C;
+  a.out = out;
+  a.tickets = nullptr;
+  a.partials = nullptr;
+  a.B = B;
+  a.K = K;
+  a.D = D;
+  a.G = 1;
+  a.rpg = K;
+  a.zscale = (float)((double)scale / (double)temperature);
+  a.cosine = sim == CS_SIM_COSINE;
+  a.staged_norms = norms;
+  const cs::LaunchShape ls = make_shape(B, K, D, 1, K, Q, C);
+  hipError_t err = cs::launch_row_norms(C, (long long)B * K, D, ls.vec, ls.nt, norms, stream);
+  if (err == hipSuccess) err = cs::launch_fused(a, ls, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return CS_ERR_LAUNCH;
@@ -237,6 +274,13 @@ int cs_score_candidates_batch(const float* queries, const float* candidates, int
   const int G = workspace != nullptr ? plan_groups(B, K, D) : 1;
   return score(queries, candidates, B, K, D, similarity, scale, temperature, out, workspace,
                workspace_bytes, G, stream);
+}
+
+int cs_score_candidates_unfused(const float* queries, const float* candidates, int B, int K,
+                                int D, int similarity, float scale, float temperature,
+                                float* out, float* row_norms, hipStream_t stream) {
+  return score_unfused(queries, candidates, B, K, D, similarity, scale, temperature, out,
+                       row_norms, stream);
 }
 
 int cs_score_candidates(const float* query, const float* candidates, int K, int D,

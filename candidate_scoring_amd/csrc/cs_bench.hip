@@ -8,6 +8,8 @@
 //
 // Entry points (all return 0 or a negative code; HIP errors are -1000 - err):
 //   csb_time_calls   events around `iters` back-to-back direct calls
+//   csb_time_calls_rotating  the same, each call on the next of several
+//                    copies of the inputs (cold caches)
 //   csb_time_graph   capture `calls_per_graph` calls into one graph, check the
 //                    node count, then events around `replays` graph launches
 //   csb_graph_nodes  capture one call and report its node count
@@ -34,7 +36,8 @@ typedef struct {
   float scale, temperature;
   void* workspace;
   size_t workspace_bytes;
-  int groups;  // <= 0: the library's own plan
+  int groups;         // <= 0: the library's own plan
+  float* row_norms;   // non-NULL: the unfused baseline (norm pass + scoring)
 } csb_call;
 
 }  // extern "C"
@@ -72,6 +75,9 @@ int hip_code(hipError_t e) { return e == hipSuccess ? 0 : -1000 - (int)e; }
   } while (0)
 
 int issue(const csb_call* c, hipStream_t s) {
+  if (c->row_norms != nullptr)
+    return cs_score_candidates_unfused(c->Q, c->C, c->B, c->K, c->D, c->similarity, c->scale,
+                                       c->temperature, c->out, c->row_norms, s);
   if (c->groups > 0)
     return cs_score_candidates_batch_groups(c->Q, c->C, c->B, c->K, c->D, c->similarity,
                                             c->scale, c->temperature, c->out, c->workspace,
@@ -142,6 +148,24 @@ extern "C" {
 
 int csb_time_calls(const csb_call* c, int iters, hipStream_t stream, float* ms) {
   return time_loop(stream, iters, [&](hipStream_t s) { return issue(c, s); }, ms);
+}
+
+// Cold-cache variant: call i reads copy (i % copies) of the inputs, the
+// copies lying q_stride / c_stride floats apart (and the output likewise
+// out_stride apart), so that repeated calls do not hit in any cache when
+// the copies together exceed the caches.
+int csb_time_calls_rotating(const csb_call* c, int copies, size_t q_stride, size_t c_stride,
+                            size_t out_stride, int iters, hipStream_t stream, float* ms) {
+  if (copies < 1) return -1;
+  int i = 0;
+  return time_loop(stream, iters, [&](hipStream_t s) {
+    csb_call k = *c;
+    const size_t j = (size_t)(i++ % copies);
+    k.Q = c->Q + j * q_stride;
+    k.C = c->C + j * c_stride;
+    k.out = c->out + j * out_stride;
+    return issue(&k, s);
+  }, ms);
 }
 
 int csb_graph_nodes(const csb_call* c, size_t* nodes) {

@@ -57,7 +57,8 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 512;        // threads per workgroup (upper bound)
 constexpr int kMaxSlots = 256;     // LDS logit slots (K <= 255)
-constexpr float kNormEps2 = 1e-24f;  // (1e-12)^2: per-norm clamp of the cosine
+constexpr float kNormEps = 1e-12f;   // per-norm clamp of the cosine
+constexpr float kNormEps2 = 1e-24f;  // its square, for clamping squared norms
 
 // ---------------------------------------------------------------------------
 // Cross-lane primitives (wave64).
@@ -254,7 +255,15 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
     const int k = lane + kWave * i;
     if (k < n) {
       float v = s.dot[k];
-      if (COS) v = v * rsqrtf(fmaxf(s.ss[k], kNormEps2));
+      if (COS) {
+        v = v * rsqrtf(fmaxf(s.ss[k], kNormEps2));
+      } else if (a.staged_norms != nullptr) {
+        // Unfused baseline: the row norm comes from the staged array that a
+        // separate pass wrote. The dot-product similarity has no use for it
+        // beyond passing on a NaN row, but still pays for loading it.
+        const float nrm = a.staged_norms[(size_t)b * (size_t)a.K + r0 + k];
+        v = a.cosine ? v / fmaxf(nrm, kNormEps) : v * (nrm >= 0.0f ? 1.0f : NAN);
+      }
       z[i] = v * zfac;
       m = fmaxf(m, z[i]);
     } else {
@@ -411,7 +420,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
     __syncthreads();
     if (wave == 0) {
       float zfac = a.zscale;
-      if (COS) {
+      if (COS || (a.cosine && a.staged_norms != nullptr)) {
         float qq = 0.0f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) qq = dot4(qr[j], qr[j], qq);
@@ -449,6 +458,7 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
     const int r1 = min(a.K, r0 + a.rpg);
     const float* qb = a.Q + (size_t)b * (size_t)a.D;
     const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
+    const bool need_qq = COS || (a.cosine && a.staged_norms != nullptr);
     float qq = 0.0f;
     for (int c0 = 0; c0 < a.D; c0 += kQChunk) {
       const int clen = min(kQChunk, a.D - c0);
@@ -459,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
       for (int i = tid; i < nv; i += blockDim.x) {
         const VecT v = qs[i];
         ql[i] = v;
-        if (COS) {
+        if (need_qq) {
           if constexpr (VEC == 4)
             qq = dot4(v, v, qq);
           else
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
       }
     }
     float zfac = a.zscale;
-    if (COS) {
+    if (need_qq) {
       const float qn2 = block_sum(qq, s.red, lane, wave, nwaves);
       zfac = a.zscale * rsqrtf(fmaxf(qn2, kNormEps2));
     } else {
@@ -516,6 +526,45 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
     if (wave == 0) slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
     if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
     __syncthreads();
+  }
+}
+
+// Unfused baseline, first pass: the Euclidean norm of every candidate row,
+// written to a staged array (R = 4 rows per wave, rows strided over waves).
+template <int VEC, bool NT>
+__global__ __launch_bounds__(256) void row_norms(const float* __restrict__ C, long long rows,
+                                                 int D, float* __restrict__ norms) {
+  using VecT = typename std::conditional<VEC == 4, float4, float>::type;
+  constexpr int R = 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const long long nwaves = ((long long)gridDim.x * blockDim.x) / kWave;
+  const int nv = D / VEC;
+  for (long long r0 = wave * R; r0 < rows; r0 += nwaves * R) {
+    float acc[R];
+    const VecT* rp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = 0.0f;
+      rp[r] = reinterpret_cast<const VecT*>(C + (size_t)min(r0 + r, rows - 1) * (size_t)D);
+    }
+    for (int i = lane; i < nv; i += kWave) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if constexpr (VEC == 4) {
+          const float4 c = load4<NT>(rp[r] + i);
+          acc[r] = dot4(c, c, acc[r]);
+        } else {
+          const float c = load1<NT>(rp[r] + i);
+          acc[r] = fmaf(c, c, acc[r]);
+        }
+      }
+    }
+    const float total = wave_reduce_transposed<R>(acc, lane, OpSum());
+    if ((lane & (kWave / R - 1)) == 0) {
+      const long long row = r0 + lane / (kWave / R);
+      if (row < rows) norms[row] = sqrtf(total);
+    }
   }
 }
 
@@ -597,7 +646,27 @@ int regq_nv_for(int D) {
 }
 
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
-  return a.cosine ? launch_cos<true>(a, ls, stream) : launch_cos<false>(a, ls, stream);
+  // With staged norms (unfused baseline) the hot loop accumulates dots only.
+  const bool accumulate_norms = a.cosine && a.staged_norms == nullptr;
+  return accumulate_norms ? launch_cos<true>(a, ls, stream) : launch_cos<false>(a, ls, stream);
+}
+
+hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,
+                            hipStream_t stream) {
+  const long long groups = (rows + 3) / 4;  // four rows per wave
+  const unsigned grid = (unsigned)std::min<long long>((groups + 3) / 4, 1 << 20);
+  if (vec == 4) {
+    if (nt)
+      hipLaunchKernelGGL((row_norms<4, true>), dim3(grid), dim3(256), 0, stream, C, rows, D, norms);
+    else
+      hipLaunchKernelGGL((row_norms<4, false>), dim3(grid), dim3(256), 0, stream, C, rows, D, norms);
+  } else {
+    if (nt)
+      hipLaunchKernelGGL((row_norms<1, true>), dim3(grid), dim3(256), 0, stream, C, rows, D, norms);
+    else
+      hipLaunchKernelGGL((row_norms<1, false>), dim3(grid), dim3(256), 0, stream, C, rows, D, norms);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {

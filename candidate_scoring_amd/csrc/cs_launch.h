@@ -21,6 +21,7 @@ struct KernelArgs {
   int rpg;             // candidates per slice: slice g owns [g*rpg, min(K,(g+1)*rpg))
   float zscale;        // scale / temperature, rounded once to fp32
   int cosine;          // 1: cosine similarity, 0: dot product
+  const float* staged_norms;  // unfused baseline: [B][K] row norms from a separate pass
 };
 
 struct LaunchShape {
@@ -38,6 +39,9 @@ int regq_nv_for(int D);
 
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+// Unfused baseline, first pass: norms[r] = |C row r| for r < rows.
+hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,
+                            hipStream_t stream);
 
 }  // namespace cs
 

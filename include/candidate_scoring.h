@@ -137,6 +137,19 @@ int cs_score_candidates_batch_groups(const float *queries, const float *candidat
                                      float temperature, float *out, void *workspace,
                                      size_t workspace_bytes, int groups, hipStream_t stream);
 
+/* Unfused baseline for A/B measurement (pull request "cuda: add a fused
+ * candidate-scoring kernel for CLM and Kev", "What it is worth": the same
+ * block with the row norm loaded from a staged array instead of accumulated
+ * beside the dot, plus a separate norm pass; Kev, which needs no norm, runs
+ * both kernels too). Enqueues two kernels on `stream`: a pass writing the
+ * norm of every candidate row to row_norms [B][K] (device, caller-owned,
+ * 4-byte aligned; CS_ERR_WORKSPACE if NULL), then one workgroup per question
+ * that loads those norms. Same arguments, checks and result as
+ * cs_score_candidates_batch(); C is read twice. */
+int cs_score_candidates_unfused(const float *queries, const float *candidates, int B, int K,
+                                int D, int similarity, float scale, float temperature,
+                                float *out, float *row_norms, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -178,3 +178,20 @@ def test_product_path_does_not_touch_the_oracle():
         assert "cso_" not in out
         deps = subprocess.run(["ldd", str(cs.LIBRARY)], capture_output=True, text=True).stdout
         assert "oracle" not in deps
+
+
+def test_unfused_rejections_before_device_work(lib):
+    q, c, out = _host_buf(8), _host_buf(32), _host_buf(64)
+    norms = _host_buf(16)
+    # missing staging buffer
+    assert lib.cs_score_candidates_unfused(q.ctypes.data, c.ctypes.data, 1, 4, 8, 0, 1.0, 1.0,
+                                           out.ctypes.data, None, None) == cs.CS_ERR_WORKSPACE
+    for origin, change, expect in rejection_cases():
+        a = dict(query=q.ctypes.data, candidates=c.ctypes.data, out=out.ctypes.data, B=1, K=4,
+                 D=8, similarity=0, scale=1.0, temperature=1.0)
+        a.update(change)
+        st = lib.cs_score_candidates_unfused(a["query"], a["candidates"], a["B"], a["K"],
+                                             a["D"], a["similarity"], a["scale"],
+                                             a["temperature"], a["out"], norms.ctypes.data, None)
+        assert st == CODE[expect], (origin, change)
+    assert np.all(out == -7.0) and np.all(norms == -7.0)

@@ -311,3 +311,51 @@ def test_streaming_paths(cs, orc, dev, B, K, D, sim, offset):
         out = cs.score(q, c, sim, scale, 1.0, use_workspace=ws)
         torch.cuda.synchronize()
         check(out.cpu().numpy(), want, f"streaming B={B} D={D} ws={ws}")
+
+
+@pytest.mark.parametrize("name", ["clm_cos_5x512", "clm_cos_64x512", "clm_cos_255x512",
+                                  "clm_cos_255x512_identical", "clm_cos_255x512_zero_row",
+                                  "clm_cos_batch8_255x512", "clm_cos_batch8_255x512_overflow",
+                                  "kev_dot_255x2560"])
+def test_unfused_baseline(cs, orc, dev, name):
+    """The unfused baseline (norm pass + scoring that loads staged norms)
+    computes the same distribution."""
+    import torch
+
+    w = workloads.make(name)
+    note(f"case unfused {name}")
+    want = orc.score(w.Q, w.C, w.similarity, w.scale, w.temperature)
+    q, c = to_dev(w.Q, dev), to_dev(w.C, dev)
+    out = torch.empty(w.B, w.K, device=dev)
+    norms = torch.full((w.B * w.K,), -1.0, device=dev)
+    st = cs.cs_score_candidates_unfused(q, c, w.B, w.K, w.D, w.similarity, float(w.scale),
+                                        float(w.temperature), out, norms)
+    assert st == 0
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), want, f"unfused {name}")
+    nref = np.linalg.norm(w.C.astype(np.float64), axis=2).reshape(-1)
+    assert np.allclose(norms.cpu().numpy(), nref, rtol=1e-5, atol=1e-30)
+    if name == "clm_cos_255x512_identical":
+        assert np.all(out.cpu().numpy() == np.float32(1.0 / 255))
+
+
+@pytest.mark.parametrize("D,offset", [(3, 0), (2560, 0), (4097, 0), (512, 1)])
+def test_unfused_general_shapes(cs, orc, dev, D, offset):
+    import torch
+
+    B, K = 3, 77
+    Q, C = workloads.normal_inputs(31, B, K, D)
+    for sim in ("cosine", "dot"):
+        want = orc.score(Q, C, sim, 3.0)
+        qd = torch.zeros(B * D + offset, device=dev)
+        cd = torch.zeros(B * K * D + offset, device=dev)
+        qd[offset:] = to_dev(Q.reshape(-1), dev)
+        cd[offset:] = to_dev(C.reshape(-1), dev)
+        out = torch.empty(B, K, device=dev)
+        norms = torch.empty(B * K, device=dev)
+        note(f"case unfused general D={D} offset={offset} {sim}")
+        st = cs.cs_score_candidates_unfused(qd[offset:], cd[offset:], B, K, D, sim, 3.0, 1.0,
+                                            out, norms)
+        assert st == 0
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), want, f"unfused D={D} {sim}")

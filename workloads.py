@@ -70,6 +70,8 @@ def normal_inputs(seed: int, B: int, K: int, D: int):
 BASE_CONFIGS = {
     "clm_cos_5x512": ("single", 1, 5, 512, "cosine", SCALE_COSINE, 1,
                       "1 question, cosine, K=5, D=512"),
+    "clm_cos_64x512": ("single", 1, 64, 512, "cosine", SCALE_COSINE, 6,
+                       "1 question, cosine, K=64, D=512"),
     "clm_cos_255x512": ("single", 1, 255, 512, "cosine", SCALE_COSINE, 2,
                         "1 question, cosine, K=255, D=512"),
     "clm_cos_batch8_255x512": ("batch", 8, 255, 512, "cosine", SCALE_COSINE, 3,
@@ -82,6 +84,11 @@ BASE_CONFIGS = {
 
 # The bandwidth-bound shape that the bench times.
 HEADLINE = "kev_dot_batch1024_255x2560"
+
+# The shapes of the page's fused-vs-unfused table ("What it is worth"), plus
+# the bandwidth-bound batch.
+AB_SHAPES = ["clm_cos_5x512", "clm_cos_64x512", "clm_cos_255x512", "clm_cos_batch8_255x512",
+             "kev_dot_255x2560", "kev_dot_batch1024_255x2560"]
 
 
 def make(name: str, B: int | None = None) -> Workload:
@@ -126,6 +133,7 @@ def make(name: str, B: int | None = None) -> Workload:
 
 ALL = [
     "clm_cos_5x512",
+    "clm_cos_64x512",
     "clm_cos_255x512",
     "clm_cos_1x512_single_candidate",
     "clm_cos_255x512_identical",
