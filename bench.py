@@ -223,6 +223,45 @@ def cold_section(devc, iters, target_bytes=768 << 20):
     return res
 
 
+def ragged_section(devc, iters=20):
+    """A ragged Kev-shaped batch: 1024 questions, counts uniform in 1..255,
+    D=2560, dot, one launch (cs_score_candidates_ragged)."""
+    torch = devc.torch
+    cs = devc.cs
+    B, D = 1024, 2560
+    offsets = workloads.ragged_offsets(61, B)
+    Q, C = workloads.ragged_inputs(67, offsets, D)
+    rows = int(offsets[-1])
+    q = torch.from_numpy(Q).to(devc.dev)
+    c = torch.from_numpy(C).to(devc.dev)
+    o = torch.from_numpy(offsets).to(devc.dev)
+    out = torch.empty(rows, dtype=torch.float32, device=devc.dev)
+    status = torch.zeros(1, dtype=torch.int32, device=devc.dev)
+
+    def once():
+        st = cs.cs_score_candidates_ragged(q, c, o, B, rows, D, "dot", float(workloads.SCALE_DOT),
+                                           1.0, out, status, devc.stream)
+        assert st == 0, st
+
+    for _ in range(3):
+        once()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(devc.stream)
+    for _ in range(iters):
+        once()
+    e1.record(devc.stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / iters
+    nbytes = 4 * (rows * D + B * D + rows)
+    assert int(status.item()) == 0
+    res = {"B": B, "rows": rows, "D": D, "similarity": "dot", "us_per_call": round(us, 2),
+           "algorithmic_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+           "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    log(f"ragged: {res}")
+    del q, c, o, out
+    return res
+
+
 def cpu_baseline(w, max_seconds=10.0):
     """The oracle as it stands, single-threaded, on the headline batch: as
     many whole passes as fit in about max_seconds (at least one)."""
@@ -264,6 +303,7 @@ def main():
     ap.add_argument("--no-latency", action="store_true", help="skip the small-shape latencies")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-ab", action="store_true", help="skip the fused vs unfused table")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -346,6 +386,8 @@ def main():
         result["cold_latency"] = cold_section(devc, 2000)
     if ab is not None:
         result["fused_vs_unfused"] = ab
+    if not args.no_ragged:
+        result["ragged"] = ragged_section(devc)
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)

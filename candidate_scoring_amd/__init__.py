@@ -73,6 +73,8 @@ def load(path: Path | str = LIBRARY):
         "cs_score_candidates_batch_groups": (
             i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, i32, vp]),
         "cs_score_candidates_unfused": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp]),
+        "cs_score_candidates_ragged": (i32, [vp, vp, vp, i32, ctypes.c_int64, i32, i32, f32, f32,
+                                             vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -221,6 +223,14 @@ def cs_score_candidates_unfused(queries, candidates, B: int, K: int, D: int, sim
     return load().cs_score_candidates_unfused(_ptr(queries), _ptr(candidates), B, K, D,
                                               _sim(similarity), scale, temperature, _ptr(out),
                                               _ptr(row_norms), _stream(stream))
+
+
+def cs_score_candidates_ragged(queries, candidates, offsets, B: int, total_rows: int, D: int,
+                               similarity, scale: float, temperature: float, out, status=None,
+                               stream=None) -> int:
+    return load().cs_score_candidates_ragged(_ptr(queries), _ptr(candidates), _ptr(offsets), B,
+                                             total_rows, D, _sim(similarity), scale, temperature,
+                                             _ptr(out), _ptr(status), _stream(stream))
 
 
 # ----------------------------------------------------------------------------

@@ -37,6 +37,10 @@ constexpr int kMaxSplitWaves = 4;  // a slice of a split question: up to 256 thr
 // G* is large enough to beat one fuller workgroup per question; measured on
 // MI355X for K = 255, D = 512 and 2560, B = 1 .. 1024, that is G* >= 5.
 constexpr double kSliceBalanceBytes = 2400.0;
+// The merge adds about 2 us (release, ticket, acquire, rescale), so a
+// question that one 8-wave workgroup streams in less than that (about
+// 160 GB/s x 2 us = 320 KB) is never split.
+constexpr double kMinSplitBytes = 320.0 * 1024;
 // Candidate blocks larger than all eight XCD L2 caches together are streamed
 // with non-temporal loads.
 constexpr double kStreamBytes = 32.0 * 1024 * 1024;
@@ -87,6 +91,7 @@ bool is_device_pointer(const void* p) {
 int plan_groups(int B, int K, int D) {
   if (K == 1) return 1;
   const double bytes_q = 4.0 * (double)K * (double)D;
+  if (bytes_q < kMinSplitBytes) return 1;
   const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
   if (g_star < kMinUsefulSlices) return 1;
   const int G = std::min({K, kMaxSlices, (int)std::lround(g_star)});
@@ -132,7 +137,7 @@ int score(const float* Q, const float* C, int B, int K, int D, int sim, float sc
       return CS_ERR_HOST_POINTER;
   }
 
-  cs::KernelArgs a;
+  cs::KernelArgs a{};  // zero: no staged norms, no offsets
   a.Q = Q;
   a.C = C;
   a.out = out;
@@ -170,7 +175,7 @@ int score_unfused(const float* Q, const float* C, int B, int K, int D, int sim, 
         !is_device_pointer(norms))
       return CS_ERR_HOST_POINTER;
   }
-  cs::KernelArgs a;
+  cs::KernelArgs a{};  // zero: no staged norms, no offsets
   a.Q = Q;
   a.C = C;
   a.out = out;
@@ -187,6 +192,47 @@ int score_unfused(const float* Q, const float* C, int B, int K, int D, int sim, 
   const cs::LaunchShape ls = make_shape(B, K, D, 1, K, Q, C);
   hipError_t err = cs::launch_row_norms(C, (long long)B * K, D, ls.vec, ls.nt, norms, stream);
   if (err == hipSuccess) err = cs::launch_fused(a, ls, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return CS_OK;
+}
+
+// Ragged batch: question b owns rows offsets[b] .. offsets[b+1]-1 of C and
+// out; one workgroup per question, which checks its own offsets.
+int score_ragged(const float* Q, const float* C, const long long* offsets, int B,
+                 long long total_rows, int D, int sim, float scale, float temperature, float* out,
+                 int* status, hipStream_t stream) {
+  if (offsets == nullptr) return CS_ERR_NULL_POINTER;
+  int st = validate(Q, C, out, B, 1, D, sim, scale, temperature);
+  if (st != CS_OK) return st;
+  // every question needs 1..255 rows
+  if (total_rows < (long long)B || total_rows > (long long)B * CS_MAX_K) return CS_ERR_K_RANGE;
+  if (debug_pointers()) {
+    if (!is_device_pointer(Q) || !is_device_pointer(C) || !is_device_pointer(out) ||
+        !is_device_pointer(offsets) || (status != nullptr && !is_device_pointer(status)))
+      return CS_ERR_HOST_POINTER;
+  }
+  cs::KernelArgs a{};
+  a.Q = Q;
+  a.C = C;
+  a.out = out;
+  a.B = B;
+  a.K = CS_MAX_K;  // upper bound; each question's own count comes from offsets
+  a.D = D;
+  a.G = 1;
+  a.rpg = CS_MAX_K;
+  a.zscale = (float)((double)scale / (double)temperature);
+  a.cosine = sim == CS_SIM_COSINE;
+  a.offsets = offsets;
+  a.total_rows = total_rows;
+  a.status = status;
+  // launch shape as for a dense batch of the same total size
+  const int mean_k = (int)std::max<long long>(1, total_rows / B);
+  cs::LaunchShape ls = make_shape(B, mean_k, D, 1, CS_MAX_K, Q, C);
+  ls.nt = 4.0 * (double)total_rows * (double)D >= kStreamBytes ? 1 : 0;
+  const hipError_t err = cs::launch_fused(a, ls, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return CS_ERR_LAUNCH;
@@ -281,6 +327,16 @@ int cs_score_candidates_unfused(const float* queries, const float* candidates, i
                                 float* out, float* row_norms, hipStream_t stream) {
   return score_unfused(queries, candidates, B, K, D, similarity, scale, temperature, out,
                        row_norms, stream);
+}
+
+int cs_score_candidates_ragged(const float* queries, const float* candidates,
+                               const int64_t* offsets, int B, int64_t total_rows, int D,
+                               int similarity, float scale, float temperature, float* out,
+                               int* status, hipStream_t stream) {
+  static_assert(sizeof(int64_t) == sizeof(long long), "offsets are 64-bit");
+  return score_ragged(queries, candidates, reinterpret_cast<const long long*>(offsets), B,
+                      (long long)total_rows, D, similarity, scale, temperature, out, status,
+                      stream);
 }
 
 int cs_score_candidates(const float* query, const float* candidates, int K, int D,

@@ -57,6 +57,8 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 512;        // threads per workgroup (upper bound)
 constexpr int kMaxSlots = 256;     // LDS logit slots (K <= 255)
+constexpr int kMaxK = 255;
+constexpr int kStatusBadOffsets = -2;  // the K-range status of the C ABI
 constexpr float kNormEps = 1e-12f;   // per-norm clamp of the cosine
 constexpr float kNormEps2 = 1e-24f;  // its square, for clamping squared norms
 
@@ -222,6 +224,33 @@ struct Lds {
   int last;
 };
 
+// Where one question's candidates and outputs live: rows row .. row+K-1 of
+// C and of out. Dense batches: row = b*K. Ragged batches: the offsets array.
+struct Question {
+  size_t row;
+  int K;
+};
+
+// Resolves question b. For a ragged batch the workgroup checks the offsets
+// it was given (0 <= lo, hi <= total rows, 1 <= hi - lo <= 255); a bad
+// question is skipped, writes nothing, and raises the caller's status word.
+__device__ __forceinline__ bool resolve_question(const KernelArgs& a, int b, int tid,
+                                                 Question& qn) {
+  if (a.offsets == nullptr) {
+    qn.row = (size_t)b * (size_t)a.K;
+    qn.K = a.K;
+    return true;
+  }
+  const long long lo = a.offsets[b], hi = a.offsets[b + 1];
+  if (!(lo >= 0 && hi <= a.total_rows && hi - lo >= 1 && hi - lo <= kMaxK)) {
+    if (tid == 0 && a.status != nullptr) *a.status = kStatusBadOffsets;
+    return false;
+  }
+  qn.row = (size_t)lo;
+  qn.K = (int)(hi - lo);
+  return true;
+}
+
 // Writes the reduced value of slot `slot` (dot for slots < R, squared norm
 // for slots >= R) of the row group starting at candidate k0.
 template <bool COS, int R>
@@ -246,8 +275,9 @@ __device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k
 // final probabilities (one slice per question) or the unnormalised e_k plus
 // the slice's (max, sum) partial.
 template <bool COS>
-__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, int b, int g,
-                                              int r0, int n, float zfac, int lane) {
+__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
+                                              int b, int g, int r0, int n, float zfac,
+                                              int lane) {
   float z[4];
   float m = -INFINITY;
 #pragma unroll
@@ -261,7 +291,7 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
         // Unfused baseline: the row norm comes from the staged array that a
         // separate pass wrote. The dot-product similarity has no use for it
         // beyond passing on a NaN row, but still pays for loading it.
-        const float nrm = a.staged_norms[(size_t)b * (size_t)a.K + r0 + k];
+        const float nrm = a.staged_norms[qn.row + r0 + k];
         v = a.cosine ? v / fmaxf(nrm, kNormEps) : v * (nrm >= 0.0f ? 1.0f : NAN);
       }
       z[i] = v * zfac;
@@ -280,7 +310,7 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
     l += e[i];
   }
   l = wave_allreduce(l, lane, OpSum());
-  float* out = a.out + (size_t)b * (size_t)a.K + r0;
+  float* out = a.out + qn.row + r0;
   if (a.G == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -299,8 +329,8 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
 
 // Called by every thread of a slice's workgroup after slice_softmax. With
 // several slices per question, the last slice to arrive merges.
-__device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, int tid,
-                                            int lane, int wave) {
+__device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Question& qn,
+                                            int b, int tid, int lane, int wave) {
   // Only wave 0 wrote global memory (e_k and the partial). It publishes them
   // at agent scope (all XCDs: L2 write-back) and draws the ticket; the
   // release fence orders the stores before the relaxed ticket increment.
@@ -317,12 +347,12 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, 
   // Last slice: acquire the other slices' stores (L2 invalidate), fetch the
   // e_k to rescale while wave 0 reads the partials.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  float* out = a.out + (size_t)b * (size_t)a.K;
+  float* out = a.out + qn.row;
   float ek[kMaxSlots / kWave];
 #pragma unroll
   for (int i = 0; i < kMaxSlots / kWave; ++i) {
     const int k = tid + (int)blockDim.x * i;
-    ek[i] = (k < a.K) ? out[k] : 0.0f;
+    ek[i] = (k < qn.K) ? out[k] : 0.0f;
   }
   if (wave == 0) {
     const float2* part = a.partials + (size_t)b * a.G;
@@ -356,7 +386,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, int b, 
 #pragma unroll
   for (int i = 0; i < kMaxSlots / kWave; ++i) {
     const int k = tid + (int)blockDim.x * i;
-    if (k < a.K) out[k] = ek[i] * s.merge[k / a.rpg];
+    if (k < qn.K) out[k] = ek[i] * s.merge[k / a.rpg];
   }
   if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -378,8 +408,10 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   const long long items = (long long)a.B * a.G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     const int b = (int)(item / a.G), g = (int)(item % a.G);
+    Question qn;
+    if (!resolve_question(a, b, tid, qn)) continue;  // uniform: one question per workgroup
     const int r0 = g * a.rpg;
-    const int r1 = min(a.K, r0 + a.rpg);
+    const int r1 = min(qn.K, r0 + a.rpg);
     const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
     float4 qr[NV];
 #pragma unroll
@@ -388,7 +420,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
       qr[j] = (FULL || idx < D4) ? q4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
+    const float* Cb = a.C + qn.row * (size_t)a.D;
     for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
       constexpr int V = COS ? 2 * R : R;
       float acc[V];
@@ -427,9 +459,9 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         qq = wave_allreduce(qq, lane, OpSum());
         zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
       }
-      slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
+      slice_softmax<COS>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
     }
-    if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
+    if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
 }
@@ -454,10 +486,12 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   const long long items = (long long)a.B * a.G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     const int b = (int)(item / a.G), g = (int)(item % a.G);
+    Question qn;
+    if (!resolve_question(a, b, tid, qn)) continue;  // uniform: one question per workgroup
     const int r0 = g * a.rpg;
-    const int r1 = min(a.K, r0 + a.rpg);
+    const int r1 = min(qn.K, r0 + a.rpg);
     const float* qb = a.Q + (size_t)b * (size_t)a.D;
-    const float* Cb = a.C + (size_t)b * (size_t)a.K * (size_t)a.D;
+    const float* Cb = a.C + qn.row * (size_t)a.D;
     const bool need_qq = COS || (a.cosine && a.staged_norms != nullptr);
     float qq = 0.0f;
     for (int c0 = 0; c0 < a.D; c0 += kQChunk) {
@@ -523,8 +557,8 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
     } else {
       __syncthreads();
     }
-    if (wave == 0) slice_softmax<COS>(s, a, b, g, r0, r1 - r0, zfac, lane);
-    if (a.G > 1) split_merge(s, a, b, tid, lane, wave);
+    if (wave == 0) slice_softmax<COS>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
+    if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
 }

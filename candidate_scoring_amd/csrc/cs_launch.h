@@ -22,6 +22,9 @@ struct KernelArgs {
   float zscale;        // scale / temperature, rounded once to fp32
   int cosine;          // 1: cosine similarity, 0: dot product
   const float* staged_norms;  // unfused baseline: [B][K] row norms from a separate pass
+  const long long* offsets;   // ragged batch: [B+1] row offsets (device); else nullptr
+  long long total_rows;       // ragged batch: rows of C and out
+  int* status;                // ragged batch: optional device status word
 };
 
 struct LaunchShape {

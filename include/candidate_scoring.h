@@ -137,6 +137,26 @@ int cs_score_candidates_batch_groups(const float *queries, const float *candidat
                                      float temperature, float *out, void *workspace,
                                      size_t workspace_bytes, int groups, hipStream_t stream);
 
+/* Ragged batch: B questions with their own candidate counts, one launch.
+ * Question b owns candidate rows offsets[b] .. offsets[b+1]-1 of
+ * candidates [total_rows][D] and the same slots of out [total_rows];
+ * queries is [B][D]. offsets is a DEVICE array of B+1 int64 values with
+ * offsets[0] = 0 and offsets[B] = total_rows; each count must lie in
+ * 1..255 (the per-question limit of "What is fused, precisely").
+ * The host checks pointers (offsets included), B, total_rows in
+ * [B, 255*B] (else CS_ERR_K_RANGE), D, similarity, scale and temperature;
+ * it cannot read device offsets without synchronizing, so each workgroup
+ * checks its own question: a question whose offsets fall outside
+ * [0, total_rows] or whose count is outside 1..255 is skipped, its output
+ * slots are left untouched, and CS_ERR_K_RANGE is stored to *status (a
+ * DEVICE int the caller sets to CS_OK beforehand; may be NULL). Each valid
+ * question's result equals cs_score_candidates() on its own rows. One
+ * workgroup per question; no workspace. */
+int cs_score_candidates_ragged(const float *queries, const float *candidates,
+                               const int64_t *offsets, int B, int64_t total_rows, int D,
+                               int similarity, float scale, float temperature, float *out,
+                               int *status, hipStream_t stream);
+
 /* Unfused baseline for A/B measurement (pull request "cuda: add a fused
  * candidate-scoring kernel for CLM and Kev", "What it is worth": the same
  * block with the row norm loaded from a staged array instead of accumulated

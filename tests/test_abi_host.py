@@ -195,3 +195,27 @@ def test_unfused_rejections_before_device_work(lib):
                                              a["temperature"], a["out"], norms.ctypes.data, None)
         assert st == CODE[expect], (origin, change)
     assert np.all(out == -7.0) and np.all(norms == -7.0)
+
+
+def test_ragged_rejections_before_device_work(lib):
+    q, c, out = _host_buf(16), _host_buf(64), _host_buf(64)
+    offs = np.array([0, 3, 8], dtype=np.int64)
+    base = dict(q=q.ctypes.data, c=c.ctypes.data, o=offs.ctypes.data, B=2, T=8, D=8, sim=0,
+                scale=1.0, temp=1.0, out=out.ctypes.data)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.cs_score_candidates_ragged(a["q"], a["c"], a["o"], a["B"], a["T"], a["D"],
+                                              a["sim"], a["scale"], a["temp"], a["out"], None,
+                                              None)
+
+    assert call(o=None) == cs.CS_ERR_NULL_POINTER
+    assert call(q=None) == cs.CS_ERR_NULL_POINTER
+    assert call(B=0) == cs.CS_ERR_BATCH
+    assert call(T=1) == cs.CS_ERR_K_RANGE        # fewer rows than questions
+    assert call(T=2 * 255 + 1) == cs.CS_ERR_K_RANGE
+    assert call(D=0) == cs.CS_ERR_D_RANGE
+    assert call(sim=5) == cs.CS_ERR_SIMILARITY
+    assert call(scale=0.0) == cs.CS_ERR_SCALE
+    assert call(temp=-1.0) == cs.CS_ERR_TEMPERATURE
+    assert np.all(out == -7.0)
