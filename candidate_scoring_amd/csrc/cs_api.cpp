@@ -41,6 +41,9 @@ constexpr double kSliceBalanceBytes = 2400.0;
 // question that one 8-wave workgroup streams in less than that (about
 // 160 GB/s x 2 us = 320 KB) is never split.
 constexpr double kMinSplitBytes = 320.0 * 1024;
+// Ragged batches with more questions than this (about one per CU) are
+// dispatched longest-first.
+constexpr int kResidentQuestions = 256;
 // Candidate blocks larger than all eight XCD L2 caches together are streamed
 // with non-temporal loads.
 constexpr double kStreamBytes = 32.0 * 1024 * 1024;
@@ -228,10 +231,16 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   a.offsets = offsets;
   a.total_rows = total_rows;
   a.status = status;
+  // More questions than resident workgroups (two 8-wave workgroups per CU):
+  // hand out the largest questions first so the batch ends evenly.
+  a.longest_first = B > kResidentQuestions ? 1 : 0;
   // launch shape as for a dense batch of the same total size
   const int mean_k = (int)std::max<long long>(1, total_rows / B);
   cs::LaunchShape ls = make_shape(B, mean_k, D, 1, CS_MAX_K, Q, C);
   ls.nt = 4.0 * (double)total_rows * (double)D >= kStreamBytes ? 1 : 0;
+  // The scheduled kernels run at three waves per SIMD; four-wave workgroups
+  // keep three of them resident per CU.
+  if (a.longest_first) ls.block = std::min<unsigned>(ls.block, 4 * kWave);
   const hipError_t err = cs::launch_fused(a, ls, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;

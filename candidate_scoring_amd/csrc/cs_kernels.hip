@@ -222,6 +222,9 @@ struct Lds {
   float merge[kMaxSlots];
   float red[kBlock / kWave];
   int last;
+  int hist[kMaxSlots];        // ragged longest-first order: questions per count
+  int wave_sum[kBlock / kWave];
+  int pick[2];
 };
 
 // Where one question's candidates and outputs live: rows row .. row+K-1 of
@@ -234,9 +237,10 @@ struct Question {
 // Resolves question b. For a ragged batch the workgroup checks the offsets
 // it was given (0 <= lo, hi <= total rows, 1 <= hi - lo <= 255); a bad
 // question is skipped, writes nothing, and raises the caller's status word.
+template <bool RAGGED>
 __device__ __forceinline__ bool resolve_question(const KernelArgs& a, int b, int tid,
                                                  Question& qn) {
-  if (a.offsets == nullptr) {
+  if constexpr (!RAGGED) {
     qn.row = (size_t)b * (size_t)a.K;
     qn.K = a.K;
     return true;
@@ -249,6 +253,74 @@ __device__ __forceinline__ bool resolve_question(const KernelArgs& a, int b, int
   qn.row = (size_t)lo;
   qn.K = (int)(hi - lo);
   return true;
+}
+
+// Sort key of a ragged question: 0 for 255 candidates ... 254 for one; an
+// invalid count sorts last (its workgroup then flags it).
+__device__ __forceinline__ int count_key(const KernelArgs& a, int b) {
+  const long long c = a.offsets[b + 1] - a.offsets[b];
+  return (c >= 1 && c <= kMaxK) ? kMaxK - (int)c : kMaxK;
+}
+
+// Longest-first schedule for a ragged batch larger than the resident
+// workgroups: the question of dispatch rank `rank` when questions are
+// ordered by decreasing candidate count, ties by index. Every workgroup
+// derives the same order from the offsets (a histogram of counts, then the
+// rank's position inside its count class), so each question is taken by
+// exactly one workgroup. Called by all threads; uses s.hist, s.wave_sum and
+// s.pick.
+__device__ __forceinline__ int question_of_rank(const KernelArgs& a, int rank, Lds& s, int tid, int lane,
+                                int wave) {
+  const int nt = blockDim.x, nwaves = nt / kWave;
+#pragma unroll 1
+  for (int i = tid; i < kMaxSlots; i += nt) s.hist[i] = 0;
+  __syncthreads();
+#pragma unroll 1
+  for (int b = tid; b < a.B; b += nt) atomicAdd(&s.hist[count_key(a, b)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int before = 0, key = 0;
+#pragma unroll 1
+    for (; key < kMaxSlots - 1 && rank >= before + s.hist[key]; ++key) before += s.hist[key];
+    s.pick[0] = key;
+    s.pick[1] = rank - before;  // position among the questions with this key
+  }
+  __syncthreads();
+  const int key = s.pick[0], j = s.pick[1];
+  // Each thread owns a contiguous run of questions; an exclusive scan of the
+  // per-thread match counts finds the run holding the j-th match.
+  const int chunk = (a.B + nt - 1) / nt;
+  const int lo = min(a.B, tid * chunk), hi = min(a.B, lo + chunk);
+  int mine = 0;
+#pragma unroll 1
+  for (int b = lo; b < hi; ++b) mine += count_key(a, b) == key;
+  int incl = mine;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += v;
+  }
+  if (lane == kWave - 1) s.wave_sum[wave] = incl;
+  __syncthreads();
+  int before = incl - mine;
+#pragma unroll 1
+  for (int w = 0; w < wave; ++w) before += s.wave_sum[w];
+  if (j >= before && j < before + mine) {
+    int seen = before;
+#pragma unroll 1
+    for (int b = lo; b < hi; ++b) {
+      if (count_key(a, b) == key) {
+        if (seen == j) s.pick[0] = b;
+        ++seen;
+      }
+    }
+  }
+  __syncthreads();
+  // The pick is the same for every lane; saying so keeps the addresses
+  // derived from it in scalar registers.
+  const int b = __builtin_amdgcn_readfirstlane(s.pick[0]);
+  __syncthreads();
+  (void)nwaves;
+  return b;
 }
 
 // Writes the reduced value of slot `slot` (dot for slots < R, squared norm
@@ -399,7 +471,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
 // hot loop; the query's squared norm is reduced once per workgroup (by wave
 // 0, which holds all of q) right before the softmax.
 
-template <bool COS, int NV, int R, bool FULL, bool NT>
+template <bool COS, int NV, int R, bool FULL, bool NT, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -407,9 +479,13 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   const int D4 = a.D >> 2;
   const long long items = (long long)a.B * a.G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
-    const int b = (int)(item / a.G), g = (int)(item % a.G);
+    int b = (int)(item / a.G);
+    if constexpr (RAGGED) {
+      if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
+    }
+    const int g = (int)(item % a.G);
     Question qn;
-    if (!resolve_question(a, b, tid, qn)) continue;  // uniform: one question per workgroup
+    if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
     const int r0 = g * a.rpg;
     const int r1 = min(qn.K, r0 + a.rpg);
     const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
@@ -474,7 +550,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
 
 constexpr int kQChunk = 8192;
 
-template <bool COS, int VEC, bool NT>
+template <bool COS, int VEC, bool NT, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   extern __shared__ float q_dyn[];
   __shared__ Lds s;
@@ -485,9 +561,13 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   const int nwaves = blockDim.x / kWave;
   const long long items = (long long)a.B * a.G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
-    const int b = (int)(item / a.G), g = (int)(item % a.G);
+    int b = (int)(item / a.G);
+    if constexpr (RAGGED) {
+      if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
+    }
+    const int g = (int)(item % a.G);
     Question qn;
-    if (!resolve_question(a, b, tid, qn)) continue;  // uniform: one question per workgroup
+    if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
     const int r0 = g * a.rpg;
     const int r1 = min(qn.K, r0 + a.rpg);
     const float* qb = a.Q + (size_t)b * (size_t)a.D;
@@ -615,48 +695,52 @@ __global__ void zero_bytes(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Launch selection.
 
-template <bool COS, int NV, int R, bool NT>
+template <bool COS, int NV, int R, bool NT, bool RAGGED>
 hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const bool full = (a.D >> 2) == NV * kWave;
   if (full)
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT>), dim3(ls.grid), dim3(ls.block), 0,
-                       stream, a);
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT, RAGGED>), dim3(ls.grid), dim3(ls.block),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT>), dim3(ls.grid), dim3(ls.block), 0,
-                       stream, a);
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT, RAGGED>), dim3(ls.grid),
+                       dim3(ls.block), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool COS, bool NT>
+template <bool COS, bool NT, bool RAGGED>
 hipError_t launch_regq(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   switch (ls.nv) {
-    case 1: return launch_regq_nv<COS, 1, 8, NT>(a, ls, stream);
-    case 2: return launch_regq_nv<COS, 2, 8, NT>(a, ls, stream);
-    case 4: return launch_regq_nv<COS, 4, 4, NT>(a, ls, stream);
-    case 6: return launch_regq_nv<COS, 6, 2, NT>(a, ls, stream);
-    case 8: return launch_regq_nv<COS, 8, 2, NT>(a, ls, stream);
-    case 10: return launch_regq_nv<COS, 10, 2, NT>(a, ls, stream);
-    case 12: return launch_regq_nv<COS, 12, 1, NT>(a, ls, stream);
-    case 16: return launch_regq_nv<COS, 16, 1, NT>(a, ls, stream);
+    case 1: return launch_regq_nv<COS, 1, 8, NT, RAGGED>(a, ls, stream);
+    case 2: return launch_regq_nv<COS, 2, 8, NT, RAGGED>(a, ls, stream);
+    case 4: return launch_regq_nv<COS, 4, 4, NT, RAGGED>(a, ls, stream);
+    case 6: return launch_regq_nv<COS, 6, 2, NT, RAGGED>(a, ls, stream);
+    case 8: return launch_regq_nv<COS, 8, 2, NT, RAGGED>(a, ls, stream);
+    case 10: return launch_regq_nv<COS, 10, 2, NT, RAGGED>(a, ls, stream);
+    case 12: return launch_regq_nv<COS, 12, 1, NT, RAGGED>(a, ls, stream);
+    case 16: return launch_regq_nv<COS, 16, 1, NT, RAGGED>(a, ls, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool COS, bool NT>
+template <bool COS, bool NT, bool RAGGED>
 hipError_t launch_general(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const size_t lds = sizeof(float) * (size_t)min(a.D, kQChunk);
   if (ls.vec == 4)
-    hipLaunchKernelGGL((fused_general<COS, 4, NT>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+    hipLaunchKernelGGL((fused_general<COS, 4, NT, RAGGED>), dim3(ls.grid), dim3(ls.block), lds,
+                       stream, a);
   else
-    hipLaunchKernelGGL((fused_general<COS, 1, NT>), dim3(ls.grid), dim3(ls.block), lds, stream, a);
+    hipLaunchKernelGGL((fused_general<COS, 1, NT, RAGGED>), dim3(ls.grid), dim3(ls.block), lds,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <bool COS>
-hipError_t launch_cos(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+template <bool COS, bool RAGGED>
+hipError_t launch_kind(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   if (ls.nv > 0)
-    return ls.nt ? launch_regq<COS, true>(a, ls, stream) : launch_regq<COS, false>(a, ls, stream);
-  return ls.nt ? launch_general<COS, true>(a, ls, stream) : launch_general<COS, false>(a, ls, stream);
+    return ls.nt ? launch_regq<COS, true, RAGGED>(a, ls, stream)
+                 : launch_regq<COS, false, RAGGED>(a, ls, stream);
+  return ls.nt ? launch_general<COS, true, RAGGED>(a, ls, stream)
+               : launch_general<COS, false, RAGGED>(a, ls, stream);
 }
 
 }  // namespace
@@ -682,7 +766,11 @@ int regq_nv_for(int D) {
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   // With staged norms (unfused baseline) the hot loop accumulates dots only.
   const bool accumulate_norms = a.cosine && a.staged_norms == nullptr;
-  return accumulate_norms ? launch_cos<true>(a, ls, stream) : launch_cos<false>(a, ls, stream);
+  if (a.offsets != nullptr)
+    return accumulate_norms ? launch_kind<true, true>(a, ls, stream)
+                            : launch_kind<false, true>(a, ls, stream);
+  return accumulate_norms ? launch_kind<true, false>(a, ls, stream)
+                          : launch_kind<false, false>(a, ls, stream);
 }
 
 hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,

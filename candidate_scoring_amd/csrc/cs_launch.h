@@ -25,6 +25,7 @@ struct KernelArgs {
   const long long* offsets;   // ragged batch: [B+1] row offsets (device); else nullptr
   long long total_rows;       // ragged batch: rows of C and out
   int* status;                // ragged batch: optional device status word
+  int longest_first;          // ragged batch: dispatch questions by decreasing count
 };
 
 struct LaunchShape {
