@@ -262,6 +262,59 @@ def ragged_section(devc, iters=20):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def projected_section(devc, iters=20):
+    """Projection + scoring on the two 1024-question head workloads (bf16
+    hidden states and heads): Kev (dot, heads 2560 -> 256, folded into the
+    query) and CLM (cosine, heads 512 -> 256, candidate projection on the
+    matrix cores). Reports us/call, HBM GB/s of the bf16 inputs and, for the
+    cosine path, the dense bf16 TFLOP/s of the projections."""
+    torch = devc.torch
+    cs = devc.cs
+    res = {}
+    for name in sorted(workloads.PROJECTED_CONFIGS):
+        w = workloads.make_projected(name)
+
+        def dev16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(devc.dev)
+
+        xq, xc, wq, wc = dev16(w.xq_bits), dev16(w.xc_bits), dev16(w.wq_bits), dev16(w.wc_bits)
+        out = torch.empty(w.B, w.K, dtype=torch.float32, device=devc.dev)
+        nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, w.similarity)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=devc.dev)
+
+        def once():
+            st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, w.similarity,
+                                       float(w.scale), 1.0, out, ws, nbytes, devc.stream)
+            assert st == 0, st
+
+        for _ in range(3):
+            once()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(devc.stream)
+        for _ in range(iters):
+            once()
+        e1.record(devc.stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / iters
+        gbs = w.algorithmic_bytes / us / 1e3
+        row = {"B": w.B, "K": w.K, "Hq": w.Hq, "Hc": w.Hc, "P": w.P, "similarity": w.similarity,
+               "dtype": "bf16 in, fp32 accumulate", "us_per_call": round(us, 2),
+               "algorithmic_bytes": w.algorithmic_bytes, "GBps": round(gbs, 1),
+               "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        if w.similarity == "cosine":
+            flops = 2.0 * w.B * (w.K * w.Hc * w.P + w.Hq * w.P)
+            tf = flops / us / 1e6
+            row.update({"flops": flops, "TFLOPs": round(tf, 1),
+                        "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        res[name] = row
+        log(f"projected {name}: {row}")
+        del xq, xc, wq, wc, out, ws
+    return res
+
+
 def cpu_baseline(w, max_seconds=10.0):
     """The oracle as it stands, single-threaded, on the headline batch: as
     many whole passes as fit in about max_seconds (at least one)."""
@@ -304,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-ab", action="store_true", help="skip the fused vs unfused table")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch")
+    ap.add_argument("--no-projected", action="store_true",
+                    help="skip the projection + scoring workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -388,6 +443,8 @@ def main():
         result["fused_vs_unfused"] = ab
     if not args.no_ragged:
         result["ragged"] = ragged_section(devc)
+    if not args.no_projected:
+        result["projected"] = projected_section(devc)
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)

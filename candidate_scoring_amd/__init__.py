@@ -36,6 +36,7 @@ CS_ERR_SIMILARITY = -7
 CS_ERR_WORKSPACE = -8
 CS_ERR_LAUNCH = -9
 CS_ERR_HOST_POINTER = -10
+CS_ERR_UNSUPPORTED = -11
 
 _lib = None
 _bench = None
@@ -73,6 +74,9 @@ def load(path: Path | str = LIBRARY):
         "cs_score_candidates_batch_groups": (
             i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, i32, vp]),
         "cs_score_candidates_unfused": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp]),
+        "cs_projected_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "cs_score_projected": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp,
+                                     vp, sz, vp]),
         "cs_score_candidates_ragged": (i32, [vp, vp, vp, i32, ctypes.c_int64, i32, i32, f32, f32,
                                              vp, vp, vp]),
     }
@@ -231,6 +235,19 @@ def cs_score_candidates_ragged(queries, candidates, offsets, B: int, total_rows:
     return load().cs_score_candidates_ragged(_ptr(queries), _ptr(candidates), _ptr(offsets), B,
                                              total_rows, D, _sim(similarity), scale, temperature,
                                              _ptr(out), _ptr(status), _stream(stream))
+
+
+def cs_projected_workspace_bytes(B: int, Hc: int, P: int, similarity) -> int:
+    return load().cs_projected_workspace_bytes(B, Hc, P, _sim(similarity))
+
+
+def cs_score_projected(xq, xc, wq, wc, B: int, K: int, Hq: int, Hc: int, P: int, similarity,
+                       scale: float, temperature: float, out, workspace, workspace_bytes: int,
+                       stream=None) -> int:
+    """bf16 tensors (torch.bfloat16 or raw uint16 device buffers)."""
+    return load().cs_score_projected(_ptr(xq), _ptr(xc), _ptr(wq), _ptr(wc), B, K, Hq, Hc, P,
+                                     _sim(similarity), scale, temperature, _ptr(out),
+                                     _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 # ----------------------------------------------------------------------------

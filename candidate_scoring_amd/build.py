@@ -62,7 +62,7 @@ def build(verbose: bool = False) -> list[Path]:
     cc = hipcc()
     tmp = LIBRARY.with_suffix(".so.tmp")
     _run([cc, *common_flags(), "-o", str(tmp), str(CSRC / "cs_kernels.hip"),
-          str(CSRC / "cs_api.cpp")], verbose)
+          str(CSRC / "cs_project.hip"), str(CSRC / "cs_api.cpp")], verbose)
     tmp.replace(LIBRARY)
     tmpb = BENCH_LIBRARY.with_suffix(".so.tmp")
     _run([cc, *common_flags(), "-o", str(tmpb), str(CSRC / "cs_bench.hip"),

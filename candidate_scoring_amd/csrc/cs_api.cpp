@@ -249,6 +249,61 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   return CS_OK;
 }
 
+size_t projected_workspace(int B, int Hc, int P, int sim) {
+  size_t bytes = align_up(sizeof(float) * (size_t)B * (size_t)P, 256);
+  if (sim == CS_SIM_DOT) bytes += sizeof(float) * (size_t)B * (size_t)Hc;
+  return bytes;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
+                    const uint16_t* wc, int B, int K, int Hq, int Hc, int P, int sim, float scale,
+                    float temperature, float* out, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (wq == nullptr || wc == nullptr) return CS_ERR_NULL_POINTER;
+  int st = validate(xq, xc, out, B, K, Hq, sim, scale, temperature);
+  if (st != CS_OK) return st;
+  if (Hc < 1 || P < 1) return CS_ERR_D_RANGE;
+  // Shapes this path implements: 16-byte bf16 pieces, at most 256 projected
+  // features; cosine tiles the features by 64, dot holds a folded query of at
+  // most 4096 floats per lane set.
+  if (Hq % 8 != 0 || Hc % 8 != 0 || P > 256 || !aligned16(xq) || !aligned16(xc) ||
+      !aligned16(wq) || !aligned16(wc))
+    return CS_ERR_UNSUPPORTED;
+  if (sim == CS_SIM_COSINE ? (P % 64 != 0) : (cs::bf16_nv_for(Hc) == 0)) return CS_ERR_UNSUPPORTED;
+  if (ws == nullptr || ws_bytes < projected_workspace(B, Hc, P, sim) || !aligned16(ws))
+    return CS_ERR_WORKSPACE;
+  if (debug_pointers()) {
+    if (!is_device_pointer(xq) || !is_device_pointer(xc) || !is_device_pointer(wq) ||
+        !is_device_pointer(wc) || !is_device_pointer(out) || !is_device_pointer(ws))
+      return CS_ERR_HOST_POINTER;
+  }
+  cs::ProjArgs p{};
+  p.xq = xq;
+  p.xc = xc;
+  p.wq = wq;
+  p.wc = wc;
+  p.out = out;
+  p.qp = static_cast<float*>(ws);
+  p.u = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                 align_up(sizeof(float) * (size_t)B * (size_t)P, 256));
+  p.B = B;
+  p.K = K;
+  p.Hq = Hq;
+  p.Hc = Hc;
+  p.P = P;
+  p.zscale = (float)((double)scale / (double)temperature);
+  p.cosine = sim == CS_SIM_COSINE;
+  p.nt = 2.0 * (double)B * (double)K * (double)Hc >= kStreamBytes ? 1 : 0;
+  const hipError_t err = cs::launch_projected(p, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return CS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +323,7 @@ const char* cs_status_string(int status) {
     case CS_ERR_WORKSPACE: return "workspace missing, too small or misaligned, or bad group count";
     case CS_ERR_LAUNCH: return "kernel launch failed";
     case CS_ERR_HOST_POINTER: return "a pointer argument is not device memory";
+    case CS_ERR_UNSUPPORTED: return "shape or alignment not implemented by this entry point";
     default: return "unknown status";
   }
 }
@@ -346,6 +402,20 @@ int cs_score_candidates_ragged(const float* queries, const float* candidates,
   return score_ragged(queries, candidates, reinterpret_cast<const long long*>(offsets), B,
                       (long long)total_rows, D, similarity, scale, temperature, out, status,
                       stream);
+}
+
+size_t cs_projected_workspace_bytes(int B, int Hc, int P, int similarity) {
+  if (B < 1 || Hc < 1 || P < 1 || (similarity != CS_SIM_DOT && similarity != CS_SIM_COSINE))
+    return 0;
+  return projected_workspace(B, Hc, P, similarity);
+}
+
+int cs_score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
+                       const uint16_t* wc, int B, int K, int Hq, int Hc, int P, int similarity,
+                       float scale, float temperature, float* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return score_projected(xq, xc, wq, wc, B, K, Hq, Hc, P, similarity, scale, temperature, out,
+                         workspace, workspace_bytes, stream);
 }
 
 int cs_score_candidates(const float* query, const float* candidates, int K, int D,

@@ -49,419 +49,11 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "cs_device.h"
 #include "cs_launch.h"
 
 namespace cs {
 namespace {
-
-constexpr int kWave = 64;
-constexpr int kBlock = 512;        // threads per workgroup (upper bound)
-constexpr int kMaxSlots = 256;     // LDS logit slots (K <= 255)
-constexpr int kMaxK = 255;
-constexpr int kStatusBadOffsets = -2;  // the K-range status of the C ABI
-constexpr float kNormEps = 1e-12f;   // per-norm clamp of the cosine
-constexpr float kNormEps2 = 1e-24f;  // its square, for clamping squared norms
-
-// ---------------------------------------------------------------------------
-// Cross-lane primitives (wave64).
-
-// DPP controls (GFX9 encoding).
-constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
-constexpr int kDppRowHalfMirror = 0x141; // lane <-> 7 - lane within 8 lanes
-constexpr int kDppRowRor8 = 0x128;       // lane <-> lane ^ 8 within 16 lanes
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// Candidate rows are read exactly once; when the block of candidates is far
-// larger than the L2 caches, loading them non-temporally keeps them from
-// evicting anything useful (the streaming read then runs at the same rate as
-// a plain read-only copy kernel).
-typedef float v4f_t __attribute__((ext_vector_type(4)));
-
-template <bool NT>
-__device__ __forceinline__ float4 load4(const float4* p) {
-  if constexpr (NT) {
-    const v4f_t v = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
-  } else {
-    return *p;
-  }
-}
-
-template <bool NT>
-__device__ __forceinline__ float load1(const float* p) {
-  if constexpr (NT)
-    return __builtin_nontemporal_load(p);
-  else
-    return *p;
-}
-
-struct OpSum {
-  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
-};
-struct OpMax {
-  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
-};
-
-// Pairs lanes l and l^32 across two registers: afterwards lanes 0..31 hold
-// op(a[l], a[l+32]) and lanes 32..63 hold op(b[l-32], b[l]).
-template <class Op>
-__device__ __forceinline__ float pair32(float a, float b, Op op) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  // Copy the two results out before reinterpreting them: bit-casting a
-  // vector element in place reads element 0 for both.
-  const unsigned r0 = r[0], r1 = r[1];
-  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
-}
-
-// Same for lanes l and l^16: rows 0 and 2 take a, rows 1 and 3 take b.
-template <class Op>
-__device__ __forceinline__ float pair16(float a, float b, Op op) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  // Copy the two results out before reinterpreting them: bit-casting a
-  // vector element in place reads element 0 for both.
-  const unsigned r0 = r[0], r1 = r[1];
-  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
-}
-
-// One halving step inside 16-lane rows through DPP: lanes whose BIT is clear
-// keep value i, the others value i + N/2, each combined with its partner's.
-template <int CTRL, int BIT, int N, int V, class Op>
-__device__ __forceinline__ void halve_dpp(float (&v)[V], int lane, Op op) {
-  if constexpr (N >= 2) {
-    const bool upper = (lane & BIT) != 0;
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const float lo = v[i], hi = v[i + N / 2];
-      const float keep = upper ? hi : lo;
-      const float send = upper ? lo : hi;
-      v[i] = op(keep, dpp_mov<CTRL>(send));
-    }
-  } else {
-    v[0] = op(v[0], dpp_mov<CTRL>(v[0]));
-  }
-}
-
-template <int N, int V, class Op>
-__device__ __forceinline__ void halve32(float (&v)[V], Op op) {
-  if constexpr (N >= 2) {
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) v[i] = pair32(v[i], v[i + N / 2], op);
-  } else {
-    v[0] = pair32(v[0], v[0], op);
-  }
-}
-
-template <int N, int V, class Op>
-__device__ __forceinline__ void halve16(float (&v)[V], Op op) {
-  if constexpr (N >= 2) {
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) v[i] = pair16(v[i], v[i + N / 2], op);
-  } else {
-    v[0] = pair16(v[0], v[0], op);
-  }
-}
-
-// Reduces V per-lane values (V a power of two, 1..64) over the 64 lanes of
-// the wave. On return every lane l holds the reduction of value index
-// l / (64 / V). Every value goes through the same lane-pairing sequence
-// (32, 16, 8, mirror-4, 2, 1), so the result for a value does not depend
-// on its index. Must be called by all 64 lanes.
-template <int V, class Op>
-__device__ __forceinline__ float wave_reduce_transposed(float (&v)[V], int lane, Op op) {
-  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-  halve32<(V >= 2 ? V : 1), V>(v, op);
-  halve16<(V >= 4 ? V / 2 : 1), V>(v, op);
-  halve_dpp<kDppRowRor8, 8, (V >= 8 ? V / 4 : 1), V>(v, lane, op);
-  halve_dpp<kDppRowHalfMirror, 4, (V >= 16 ? V / 8 : 1), V>(v, lane, op);
-  halve_dpp<kDppQuadXor2, 2, (V >= 32 ? V / 16 : 1), V>(v, lane, op);
-  halve_dpp<kDppQuadXor1, 1, (V >= 64 ? V / 32 : 1), V>(v, lane, op);
-  return v[0];
-}
-
-template <class Op>
-__device__ __forceinline__ float wave_allreduce(float x, int lane, Op op) {
-  float v[1] = {x};
-  return wave_reduce_transposed<1>(v, lane, op);
-}
-
-// Workgroup sum in a fixed order (waves 0, 1, ...). Ends with a barrier
-// after which `scratch` may be reused.
-__device__ __forceinline__ float block_sum(float x, float* scratch, int lane, int wave,
-                                           int nwaves) {
-  x = wave_allreduce(x, lane, OpSum());
-  if (lane == 0) scratch[wave] = x;
-  __syncthreads();
-  float t = 0.0f;
-  for (int w = 0; w < nwaves; ++w) t += scratch[w];
-  __syncthreads();
-  return t;
-}
-
-__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
-  acc = fmaf(a.x, b.x, acc);
-  acc = fmaf(a.y, b.y, acc);
-  acc = fmaf(a.z, b.z, acc);
-  acc = fmaf(a.w, b.w, acc);
-  return acc;
-}
-
-// ---------------------------------------------------------------------------
-// Per-workgroup state shared by the kernel variants.
-
-struct Lds {
-  float dot[kMaxSlots];
-  float ss[kMaxSlots];
-  float merge[kMaxSlots];
-  float red[kBlock / kWave];
-  int last;
-  int hist[kMaxSlots];        // ragged longest-first order: questions per count
-  int wave_sum[kBlock / kWave];
-  int pick[2];
-};
-
-// Where one question's candidates and outputs live: rows row .. row+K-1 of
-// C and of out. Dense batches: row = b*K. Ragged batches: the offsets array.
-struct Question {
-  size_t row;
-  int K;
-};
-
-// Resolves question b. For a ragged batch the workgroup checks the offsets
-// it was given (0 <= lo, hi <= total rows, 1 <= hi - lo <= 255); a bad
-// question is skipped, writes nothing, and raises the caller's status word.
-template <bool RAGGED>
-__device__ __forceinline__ bool resolve_question(const KernelArgs& a, int b, int tid,
-                                                 Question& qn) {
-  if constexpr (!RAGGED) {
-    qn.row = (size_t)b * (size_t)a.K;
-    qn.K = a.K;
-    return true;
-  }
-  const long long lo = a.offsets[b], hi = a.offsets[b + 1];
-  if (!(lo >= 0 && hi <= a.total_rows && hi - lo >= 1 && hi - lo <= kMaxK)) {
-    if (tid == 0 && a.status != nullptr) *a.status = kStatusBadOffsets;
-    return false;
-  }
-  qn.row = (size_t)lo;
-  qn.K = (int)(hi - lo);
-  return true;
-}
-
-// Sort key of a ragged question: 0 for 255 candidates ... 254 for one; an
-// invalid count sorts last (its workgroup then flags it).
-__device__ __forceinline__ int count_key(const KernelArgs& a, int b) {
-  const long long c = a.offsets[b + 1] - a.offsets[b];
-  return (c >= 1 && c <= kMaxK) ? kMaxK - (int)c : kMaxK;
-}
-
-// Longest-first schedule for a ragged batch larger than the resident
-// workgroups: the question of dispatch rank `rank` when questions are
-// ordered by decreasing candidate count, ties by index. Every workgroup
-// derives the same order from the offsets (a histogram of counts, then the
-// rank's position inside its count class), so each question is taken by
-// exactly one workgroup. Called by all threads; uses s.hist, s.wave_sum and
-// s.pick.
-__device__ __forceinline__ int question_of_rank(const KernelArgs& a, int rank, Lds& s, int tid, int lane,
-                                int wave) {
-  const int nt = blockDim.x, nwaves = nt / kWave;
-#pragma unroll 1
-  for (int i = tid; i < kMaxSlots; i += nt) s.hist[i] = 0;
-  __syncthreads();
-#pragma unroll 1
-  for (int b = tid; b < a.B; b += nt) atomicAdd(&s.hist[count_key(a, b)], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int before = 0, key = 0;
-#pragma unroll 1
-    for (; key < kMaxSlots - 1 && rank >= before + s.hist[key]; ++key) before += s.hist[key];
-    s.pick[0] = key;
-    s.pick[1] = rank - before;  // position among the questions with this key
-  }
-  __syncthreads();
-  const int key = s.pick[0], j = s.pick[1];
-  // Each thread owns a contiguous run of questions; an exclusive scan of the
-  // per-thread match counts finds the run holding the j-th match.
-  const int chunk = (a.B + nt - 1) / nt;
-  const int lo = min(a.B, tid * chunk), hi = min(a.B, lo + chunk);
-  int mine = 0;
-#pragma unroll 1
-  for (int b = lo; b < hi; ++b) mine += count_key(a, b) == key;
-  int incl = mine;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int v = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += v;
-  }
-  if (lane == kWave - 1) s.wave_sum[wave] = incl;
-  __syncthreads();
-  int before = incl - mine;
-#pragma unroll 1
-  for (int w = 0; w < wave; ++w) before += s.wave_sum[w];
-  if (j >= before && j < before + mine) {
-    int seen = before;
-#pragma unroll 1
-    for (int b = lo; b < hi; ++b) {
-      if (count_key(a, b) == key) {
-        if (seen == j) s.pick[0] = b;
-        ++seen;
-      }
-    }
-  }
-  __syncthreads();
-  // The pick is the same for every lane; saying so keeps the addresses
-  // derived from it in scalar registers.
-  const int b = __builtin_amdgcn_readfirstlane(s.pick[0]);
-  __syncthreads();
-  (void)nwaves;
-  return b;
-}
-
-// Writes the reduced value of slot `slot` (dot for slots < R, squared norm
-// for slots >= R) of the row group starting at candidate k0.
-template <bool COS, int R>
-__device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k0, int r0,
-                                            int r1) {
-  constexpr int V = COS ? 2 * R : R;
-  constexpr int kLanesPerSlot = kWave / V;
-  if ((lane & (kLanesPerSlot - 1)) == 0) {
-    const int slot = lane / kLanesPerSlot;
-    const int r = slot % R;
-    const int k = k0 + r;
-    if (k < r1) {
-      if (slot < R)
-        s.dot[k - r0] = total;
-      else
-        s.ss[k - r0] = total;
-    }
-  }
-}
-
-// Softmax of this slice's n logits (wave 0 only) and the store of either the
-// final probabilities (one slice per question) or the unnormalised e_k plus
-// the slice's (max, sum) partial.
-template <bool COS>
-__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
-                                              int b, int g, int r0, int n, float zfac,
-                                              int lane) {
-  float z[4];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k = lane + kWave * i;
-    if (k < n) {
-      float v = s.dot[k];
-      if (COS) {
-        v = v * rsqrtf(fmaxf(s.ss[k], kNormEps2));
-      } else if (a.staged_norms != nullptr) {
-        // Unfused baseline: the row norm comes from the staged array that a
-        // separate pass wrote. The dot-product similarity has no use for it
-        // beyond passing on a NaN row, but still pays for loading it.
-        const float nrm = a.staged_norms[qn.row + r0 + k];
-        v = a.cosine ? v / fmaxf(nrm, kNormEps) : v * (nrm >= 0.0f ? 1.0f : NAN);
-      }
-      z[i] = v * zfac;
-      m = fmaxf(m, z[i]);
-    } else {
-      z[i] = -INFINITY;
-    }
-  }
-  m = wave_allreduce(m, lane, OpMax());
-  float e[4];
-  float l = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k = lane + kWave * i;
-    e[i] = (k < n) ? expf(z[i] - m) : 0.0f;
-    l += e[i];
-  }
-  l = wave_allreduce(l, lane, OpSum());
-  float* out = a.out + qn.row + r0;
-  if (a.G == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = lane + kWave * i;
-      if (k < n) out[k] = e[i] / l;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = lane + kWave * i;
-      if (k < n) out[k] = e[i];
-    }
-    if (lane == 0) a.partials[(size_t)b * a.G + g] = make_float2(m, l);
-  }
-}
-
-// Called by every thread of a slice's workgroup after slice_softmax. With
-// several slices per question, the last slice to arrive merges.
-__device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Question& qn,
-                                            int b, int tid, int lane, int wave) {
-  // Only wave 0 wrote global memory (e_k and the partial). It publishes them
-  // at agent scope (all XCDs: L2 write-back) and draws the ticket; the
-  // release fence orders the stores before the relaxed ticket increment.
-  if (wave == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane == 0) {
-      const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      s.last = (t == (unsigned)(a.G - 1));
-    }
-  }
-  __syncthreads();
-  if (!s.last) return;  // uniform across the workgroup
-  // Last slice: acquire the other slices' stores (L2 invalidate), fetch the
-  // e_k to rescale while wave 0 reads the partials.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  float* out = a.out + qn.row;
-  float ek[kMaxSlots / kWave];
-#pragma unroll
-  for (int i = 0; i < kMaxSlots / kWave; ++i) {
-    const int k = tid + (int)blockDim.x * i;
-    ek[i] = (k < qn.K) ? out[k] : 0.0f;
-  }
-  if (wave == 0) {
-    const float2* part = a.partials + (size_t)b * a.G;
-    float mg[4], lg[4];
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = lane + kWave * i;
-      const float2 v = (g < a.G) ? part[g] : make_float2(-INFINITY, 0.0f);
-      mg[i] = v.x;
-      lg[i] = v.y;
-      M = fmaxf(M, mg[i]);
-    }
-    M = wave_allreduce(M, lane, OpMax());
-    float w[4];
-    float L = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = lane + kWave * i;
-      w[i] = (g < a.G) ? expf(mg[i] - M) : 0.0f;
-      L += lg[i] * w[i];
-    }
-    L = wave_allreduce(L, lane, OpSum());
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = lane + kWave * i;
-      if (g < a.G) s.merge[g] = w[i] / L;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kMaxSlots / kWave; ++i) {
-    const int k = tid + (int)blockDim.x * i;
-    if (k < qn.K) out[k] = ek[i] * s.merge[k / a.rpg];
-  }
-  if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ---------------------------------------------------------------------------
 // Register-query kernel: D % 4 == 0, 16-byte aligned rows, D <= 256 * NV.

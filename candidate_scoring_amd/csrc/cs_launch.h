@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
+#include <stdint.h>
 
 namespace cs {
 
@@ -42,6 +43,26 @@ int regq_rows_per_wave(int nv);
 int regq_nv_for(int D);
 
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream);
+
+// Projection + scoring (bf16 inputs as raw 16-bit patterns).
+struct ProjArgs {
+  const uint16_t* xq;  // [B][Hq] query hidden states
+  const uint16_t* xc;  // [B][K][Hc] candidate hidden states
+  const uint16_t* wq;  // [P][Hq] query head
+  const uint16_t* wc;  // [P][Hc] candidate head
+  float* out;          // [B][K]
+  float* qp;           // workspace [B][P]: projected queries
+  float* u;            // workspace [B][Hc]: folded queries (dot only)
+  int B, K, Hq, Hc, P;
+  float zscale;        // scale / temperature
+  int cosine;
+  int nt;              // stream the candidate rows non-temporally
+};
+// 16-byte pieces per lane of the bf16 dot kernel for Hc (Hc % 8 == 0); 0 if
+// Hc is too large.
+int bf16_nv_for(int Hc);
+int bf16_rows_per_wave(int nv);
+hipError_t launch_projected(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // Unfused baseline, first pass: norms[r] = |C row r| for r < rows.
 hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,

@@ -79,6 +79,7 @@ extern "C" {
 #define CS_ERR_WORKSPACE (-8)    /* workspace too small or not 8-byte aligned; bad groups */
 #define CS_ERR_LAUNCH (-9)       /* the kernel launch failed; see cs_last_hip_error() */
 #define CS_ERR_HOST_POINTER (-10) /* only with CS_DEBUG_POINTERS=1: a pointer is not device memory */
+#define CS_ERR_UNSUPPORTED (-11) /* valid sizes this entry point does not implement (see its comment) */
 
 /* Returns CS_ABI_VERSION. */
 int cs_abi_version(void);
@@ -156,6 +157,30 @@ int cs_score_candidates_ragged(const float *queries, const float *candidates,
                                const int64_t *offsets, int B, int64_t total_rows, int D,
                                int similarity, float scale, float temperature, float *out,
                                int *status, hipStream_t stream);
+
+/* Projection + scoring: the caller-side heads fused with the scoring
+ * (intro table of the page: CLM's state_head / action_head ahead of the
+ * cosine, Kev's q() / k() ahead of the dot with scale 1/sqrt(256)). Each head
+ * is a linear map without bias: q'_b = Wq x_q[b] (P features from Hq) and
+ * c'_bk = Wc x_c[b][k] (P features from Hc); the result is the softmax of
+ * scale * s(q'_b, c'_bk) / temperature over each question's K candidates, as
+ * cs_score_candidates_batch() would give on the projected vectors.
+ * All inputs are bf16 (raw 16-bit patterns) in DEVICE memory, row-major:
+ * xq [B][Hq], xc [B][K][Hc], wq [P][Hq], wc [P][Hc]; out [B][K] is fp32.
+ * Accumulation is fp32. For dot, the candidate head is folded into the query
+ * (c' . q' = x . (Wc^T q')), so candidates are read once and never projected;
+ * for cosine, each question's projected candidates are computed on the
+ * matrix cores and reduced to their similarity in registers. The workspace
+ * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected (and
+ * folded) queries. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
+ * 16-byte aligned inputs, P a multiple of 64 for cosine, Hc <= 4096 for dot;
+ * other valid sizes return CS_ERR_UNSUPPORTED. Enqueues two (cosine) or
+ * three (dot) kernels on `stream`. */
+size_t cs_projected_workspace_bytes(int B, int Hc, int P, int similarity);
+int cs_score_projected(const uint16_t *xq, const uint16_t *xc, const uint16_t *wq,
+                       const uint16_t *wc, int B, int K, int Hq, int Hc, int P, int similarity,
+                       float scale, float temperature, float *out, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /* Unfused baseline for A/B measurement (pull request "cuda: add a fused
  * candidate-scoring kernel for CLM and Kev", "What it is worth": the same

@@ -219,3 +219,40 @@ def test_ragged_rejections_before_device_work(lib):
     assert call(scale=0.0) == cs.CS_ERR_SCALE
     assert call(temp=-1.0) == cs.CS_ERR_TEMPERATURE
     assert np.all(out == -7.0)
+
+
+def test_projected_rejections_before_device_work(lib):
+    xq, xc = np.zeros(64, np.uint16), np.zeros(4 * 64, np.uint16)
+    wq, wc = np.zeros(64 * 64, np.uint16), np.zeros(64 * 64, np.uint16)
+    out = _host_buf(16)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsp = (ws.ctypes.data + 255) // 256 * 256
+    base = dict(xq=xq.ctypes.data, xc=xc.ctypes.data, wq=wq.ctypes.data, wc=wc.ctypes.data, B=1,
+                K=4, Hq=64, Hc=64, P=64, sim=1, scale=1.0, T=1.0, out=out.ctypes.data, ws=wsp,
+                nbytes=4096)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.cs_score_projected(a["xq"], a["xc"], a["wq"], a["wc"], a["B"], a["K"], a["Hq"],
+                                      a["Hc"], a["P"], a["sim"], a["scale"], a["T"], a["out"],
+                                      a["ws"], a["nbytes"], None)
+
+    assert call(wq=None) == cs.CS_ERR_NULL_POINTER
+    assert call(xq=None) == cs.CS_ERR_NULL_POINTER
+    assert call(K=256) == cs.CS_ERR_K_RANGE
+    assert call(K=0) == cs.CS_ERR_K_RANGE
+    assert call(Hq=0) == cs.CS_ERR_D_RANGE
+    assert call(Hc=0) == cs.CS_ERR_D_RANGE
+    assert call(P=0) == cs.CS_ERR_D_RANGE
+    assert call(scale=0.0) == cs.CS_ERR_SCALE
+    assert call(T=-2.0) == cs.CS_ERR_TEMPERATURE
+    assert call(Hq=60) == cs.CS_ERR_UNSUPPORTED          # not a multiple of 8
+    assert call(P=300) == cs.CS_ERR_UNSUPPORTED          # more than 256 features
+    assert call(P=96) == cs.CS_ERR_UNSUPPORTED           # cosine tiles features by 64
+    assert call(sim=0, Hc=4104) == cs.CS_ERR_UNSUPPORTED  # folded query too long
+    assert call(xc=xc.ctypes.data + 2) == cs.CS_ERR_UNSUPPORTED
+    assert call(ws=None) == cs.CS_ERR_WORKSPACE
+    assert call(nbytes=cs.cs_projected_workspace_bytes(1, 64, 64, 1) - 1) == cs.CS_ERR_WORKSPACE
+    assert np.all(out == -7.0)
+    assert cs.cs_projected_workspace_bytes(2, 64, 64, "dot") > cs.cs_projected_workspace_bytes(
+        2, 64, 64, "cosine") > 0

@@ -1,0 +1,115 @@
+"""Projection + scoring: the caller-side heads fused with the scoring.
+
+Source: pull request "cuda: add a fused candidate-scoring kernel for CLM and
+Kev", intro table (CLM: exp(logit_scale) * cos(state_head(s),
+action_head(c)); Kev: k(h_opts) . q(h_decide) / sqrt(256)). Inputs are bf16;
+the oracle (cso_score_projected) gets the same values as fp32 and works in
+double. Bar: 1e-4 per probability, as for the plain scoring.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def to_dev16(bits, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+
+def run(cs, w, dev, T=1.0):
+    import torch
+
+    xq, xc = to_dev16(w.xq_bits, dev), to_dev16(w.xc_bits, dev)
+    wq, wc = to_dev16(w.wq_bits, dev), to_dev16(w.wc_bits, dev)
+    out = torch.full((w.B, w.K), -3.0, device=dev)
+    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, w.similarity)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, w.similarity,
+                               float(w.scale), T, out, ws, nbytes)
+    assert st == 0, st
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def want(orc, w, T=1.0, questions=None):
+    idx = slice(None) if questions is None else questions
+    return orc.score_projected(w.f32("xq")[idx], w.f32("wq"), w.f32("xc")[idx], w.f32("wc"),
+                               w.similarity, w.scale, T)
+
+
+def check(p, ref, label):
+    err = float(np.max(np.abs(p.astype(np.float64) - ref)))
+    sums = float(np.max(np.abs(p.astype(np.float64).sum(axis=-1) - 1.0)))
+    note(f"  {label}: max|gpu-oracle|={err:.3e} max|rowsum-1|={sums:.3e}")
+    assert np.all(np.isfinite(p)) and err <= TOL and sums <= 1e-5, label
+
+
+@pytest.fixture(scope="module")
+def dev(cs):
+    import torch
+
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("B,K,Hq,Hc,P,sim", [
+    (4, 255, 2560, 2560, 256, "dot"),      # Kev-shaped heads
+    (4, 255, 512, 512, 256, "cosine"),     # CLM-shaped heads
+    (3, 255, 512, 512, 64, "cosine"),
+    (3, 200, 256, 520, 128, "cosine"),     # hidden not a multiple of the 64-wide chunk
+    (2, 64, 128, 1000, 192, "cosine"),
+    (5, 5, 64, 24, 64, "cosine"),
+    (2, 1, 64, 64, 64, "cosine"),
+    (3, 77, 520, 1000, 96, "dot"),
+    (2, 255, 8, 8, 8, "dot"),
+    (2, 100, 136, 4096, 256, "dot"),
+])
+def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
+    w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
+    note(f"case projected B={B} K={K} Hq={Hq} Hc={Hc} P={P} {sim}")
+    check(run(cs, w, dev), want(orc, w), f"B={B} K={K} Hc={Hc} P={P} {sim}")
+
+
+def test_projected_temperature(cs, orc, dev):
+    w = workloads.projected_inputs(91, 2, 50, 64, 64, 64, "cosine")
+    for T in (0.5, 3.0):
+        check(run(cs, w, dev, T), want(orc, w, T), f"T={T}")
+
+
+def test_projected_identical_and_zero_candidates(cs, orc, dev):
+    """Identical candidate rows give exactly 1/K on the matrix-core path (every
+    row goes through the same MFMA and reduction order); a zero candidate
+    scores a cosine of exactly 0."""
+    w = workloads.projected_inputs(93, 2, 255, 512, 512, 256, "cosine")
+    w.xc_bits[0] = w.xc_bits[0, :1]
+    w.xc_bits[1, 17] = 0
+    p = run(cs, w, dev)
+    check(p, want(orc, w), "identical/zero")
+    assert np.all(p[0] == np.float32(1.0 / 255))
+    z = orc.score_projected(w.f32("xq")[1:], w.f32("wq"), w.f32("xc")[1:], w.f32("wc"), "cosine",
+                            w.scale)
+    assert abs(float(p[1, 17]) - z[0, 17]) <= TOL
+
+
+@pytest.mark.parametrize("name", sorted(workloads.PROJECTED_CONFIGS))
+def test_projected_full_size_sampled(cs, orc, dev, name):
+    """The bench's 1024-question projected workloads at full size, in the
+    launch configuration it times; the oracle checks sampled questions."""
+    w = workloads.make_projected(name)
+    note(f"case projected full size {name}")
+    p = run(cs, w, dev)
+    sample = [0, 511, 1023]
+    check(p[sample], want(orc, w, questions=sample), f"{name} sampled")
+    sums = np.abs(p.astype(np.float64).sum(axis=1) - 1.0)
+    assert float(sums.max()) <= 1e-5

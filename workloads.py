@@ -160,3 +160,88 @@ def ragged_inputs(seed: int, offsets: np.ndarray, D: int):
     Q = rng.standard_normal((B, D), dtype=np.float32)
     C = rng.standard_normal((int(offsets[-1]), D), dtype=np.float32)
     return Q, C
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16 (ties to even); returns the 16-bit
+    patterns as uint16."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    # uint32 arithmetic: only NaN patterns could wrap, and inputs hold none
+    rounded = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """The fp32 values of bf16 patterns (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Projected:
+    """Inputs of projection + scoring: hidden states and head weights, bf16.
+    ``*_bits`` are the uint16 patterns the GPU reads; ``*_f32`` the same
+    values as fp32 for the oracle."""
+    name: str
+    similarity: str
+    scale: np.float32
+    xq_bits: np.ndarray   # [B, Hq]
+    xc_bits: np.ndarray   # [B, K, Hc]
+    wq_bits: np.ndarray   # [P, Hq]
+    wc_bits: np.ndarray   # [P, Hc]
+
+    def f32(self, which: str) -> np.ndarray:
+        return bf16_bits_to_f32(getattr(self, which + "_bits"))
+
+    @property
+    def B(self) -> int:
+        return self.xc_bits.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.xc_bits.shape[1]
+
+    @property
+    def Hc(self) -> int:
+        return self.xc_bits.shape[2]
+
+    @property
+    def Hq(self) -> int:
+        return self.xq_bits.shape[1]
+
+    @property
+    def P(self) -> int:
+        return self.wc_bits.shape[0]
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """bf16 inputs read once (hidden states and both heads), fp32 out."""
+        return 2 * (self.B * self.K * self.Hc + self.B * self.Hq + self.P * (self.Hq + self.Hc)) \
+            + 4 * self.B * self.K
+
+
+def projected_inputs(seed: int, B: int, K: int, Hq: int, Hc: int, P: int, similarity: str,
+                     scale=None, name: str = "projected") -> Projected:
+    """Hidden states N(0,1) and head weights N(0, 1/H) (so projected features
+    are O(1)), drawn in the order xq, xc, wq, wc and rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    xq = rng.standard_normal((B, Hq), dtype=np.float32)
+    xc = rng.standard_normal((B, K, Hc), dtype=np.float32)
+    wq = rng.standard_normal((P, Hq), dtype=np.float32) * np.float32(1.0 / math.sqrt(Hq))
+    wc = rng.standard_normal((P, Hc), dtype=np.float32) * np.float32(1.0 / math.sqrt(Hc))
+    if scale is None:
+        scale = SCALE_COSINE if similarity == "cosine" else SCALE_DOT
+    return Projected(name, similarity, np.float32(scale), to_bf16_bits(xq), to_bf16_bits(xc),
+                     to_bf16_bits(wq), to_bf16_bits(wc))
+
+
+# Projection workloads: Kev's heads map a 2560-wide hidden state to 256
+# features (the 1/sqrt(256) scale); CLM's map 512 to 256.
+PROJECTED_CONFIGS = {
+    "kev_proj_dot_batch1024_255x2560_p256": (1024, 255, 2560, 2560, 256, "dot", 7),
+    "clm_proj_cos_batch1024_255x512_p256": (1024, 255, 512, 512, 256, "cosine", 8),
+}
+
+
+def make_projected(name: str, B: int | None = None) -> Projected:
+    B0, K, Hq, Hc, P, sim, seed = PROJECTED_CONFIGS[name]
+    return projected_inputs(seed, B0 if B is None else B, K, Hq, Hc, P, sim, name=name)
