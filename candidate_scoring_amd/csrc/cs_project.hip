@@ -48,19 +48,6 @@ __device__ __forceinline__ uint4 load_piece(const uint16_t* p) {
                     __float_as_uint(f.w));
 }
 
-// 8 bf16 times 8 bf16, accumulated in order.
-__device__ __forceinline__ float dot8_bb(uint4 x, uint4 w, float acc) {
-  acc = fmaf(bf_lo(x.x), bf_lo(w.x), acc);
-  acc = fmaf(bf_hi(x.x), bf_hi(w.x), acc);
-  acc = fmaf(bf_lo(x.y), bf_lo(w.y), acc);
-  acc = fmaf(bf_hi(x.y), bf_hi(w.y), acc);
-  acc = fmaf(bf_lo(x.z), bf_lo(w.z), acc);
-  acc = fmaf(bf_hi(x.z), bf_hi(w.z), acc);
-  acc = fmaf(bf_lo(x.w), bf_lo(w.w), acc);
-  acc = fmaf(bf_hi(x.w), bf_hi(w.w), acc);
-  return acc;
-}
-
 // 8 bf16 times 8 fp32, accumulated in order.
 __device__ __forceinline__ float dot8_bf(uint4 x, const float (&u)[8], float acc) {
   acc = fmaf(bf_lo(x.x), u[0], acc);
@@ -89,64 +76,108 @@ __device__ __forceinline__ float halfwave_reduce_transposed(float (&v)[V], int l
 
 // ---------------------------------------------------------------------------
 // q'[b][p] = sum_h x[b][h] * w[p][h]  (x [B][H], w [P][H], bf16; H % 8 == 0).
-// A wave takes one question and 64 outputs; the query row is a broadcast
-// load, each lane streams one weight row (L1/L2 resident across questions).
+// A wave computes an 8-question x 8-output tile: lane l reads 16-byte pieces
+// 8l, 8l + 512, ... of the 8 query rows and the 8 weight rows (every load a
+// contiguous 1 KiB across the wave), accumulates the 64 partial dots, and one
+// transposed 64-value reduction leaves output (l / 8, l % 8) in lane l.
 __global__ __launch_bounds__(256) void proj_query(const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ w,
                                                   float* __restrict__ q, int B, int H, int P) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int p = blockIdx.x * kWave + lane;
-  const uint16_t* wr = w + (size_t)min(p, P - 1) * (size_t)H;
-  for (int b = blockIdx.y * 4 + wave; b < B; b += gridDim.y * 4) {  // uniform per wave
-    const uint16_t* xr = x + (size_t)b * (size_t)H;
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int h = 0; h < H; h += 8)
-      acc = dot8_bb(load_piece<false>(xr + h), load_piece<false>(wr + h), acc);
-    if (p < P) q[(size_t)b * (size_t)P + p] = acc;
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long wid = (long long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int ptiles = (P + 7) / 8;
+  const long long b0 = (wid / ptiles) * 8;
+  const int p0 = (int)(wid % ptiles) * 8;
+  if (b0 >= B) return;  // uniform across the wave
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0.0f;
+  for (int h = 8 * lane; h < H; h += 8 * kWave) {
+    float wf[8][8];
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const uint4 v = (p0 + pp < P) ? load_piece<false>(w + (size_t)(p0 + pp) * (size_t)H + h)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+      wf[pp][0] = bf_lo(v.x); wf[pp][1] = bf_hi(v.x); wf[pp][2] = bf_lo(v.y); wf[pp][3] = bf_hi(v.y);
+      wf[pp][4] = bf_lo(v.z); wf[pp][5] = bf_hi(v.z); wf[pp][6] = bf_lo(v.w); wf[pp][7] = bf_hi(v.w);
+    }
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const uint4 v = (b0 + bb < B) ? load_piece<false>(x + (size_t)(b0 + bb) * (size_t)H + h)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+      const float xf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+#pragma unroll
+      for (int pp = 0; pp < 8; ++pp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * bb + pp] = fmaf(xf[e], wf[pp][e], acc[8 * bb + pp]);
+    }
   }
+  const float total = wave_reduce_transposed<64>(acc, lane, OpSum());
+  const long long b = b0 + lane / 8;
+  const int p = p0 + lane % 8;
+  if (b < B && p < P) q[(size_t)b * (size_t)P + p] = total;
 }
 
-// u[b][h] = sum_p q'[b][p] * w[p][h]  (q' [B][P] fp32, w [P][H] bf16, P <= 256,
-// H % 4 == 0). A workgroup takes 8 questions (q' staged in LDS) and 1024
-// consecutive h, four per thread.
+// u[b][h] = sum_p q'[b][p] * w[p][h]  (q' [B][P] fp32, w [P][H] bf16,
+// P <= 256, H % 8 == 0). A workgroup computes 4 questions x 512 consecutive
+// h; lane l owns h = 8l .. 8l+7. The feature sum is split over the 4 waves
+// (wave w takes features p = w, w+4, ...), each reading one 16-byte piece of
+// weight row p per step (1 KiB contiguous across the wave) and the 4
+// questions' q'[.][p] as one broadcast LDS read; the four partial sums are
+// then added in wave order through LDS.
 __global__ __launch_bounds__(256) void fold_query(const float* __restrict__ q,
                                                   const uint16_t* __restrict__ w,
                                                   float* __restrict__ u, int B, int H, int P) {
-  __shared__ float qs[8][256];
-  const int t = threadIdx.x;
-  const int h = (blockIdx.x * 256 + t) * 4;
-  for (int b0 = blockIdx.y * 8; b0 < B; b0 += gridDim.y * 8) {  // uniform per workgroup
-    __syncthreads();  // the previous questions' q' is no longer read
-    for (int i = t; i < 8 * P; i += 256) {
-      const int bb = i / P, pp = i % P;
-      qs[bb][pp] = (b0 + bb < B) ? q[(size_t)(b0 + bb) * (size_t)P + pp] : 0.0f;
-    }
-    __syncthreads();
-    if (h >= H) continue;
-    float acc[8][4];
+  __shared__ float4 qs[256];              // q'[b0 .. b0+3][p] as one float4 per p
+  __shared__ float part[4][4][8][kWave];  // [wave][question][element][lane]
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int htiles = (H + 8 * kWave - 1) / (8 * kWave);
+  const long long b0 = ((long long)blockIdx.x / htiles) * 4;
+  const int h = (int)(blockIdx.x % htiles) * 8 * kWave + 8 * lane;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    float v[4];
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[bb][c] = 0.0f;
-    for (int p = 0; p < P; ++p) {
-      const uint2 wv = *reinterpret_cast<const uint2*>(w + (size_t)p * (size_t)H + h);
-      const float w0 = bf_lo(wv.x), w1 = bf_hi(wv.x), w2 = bf_lo(wv.y), w3 = bf_hi(wv.y);
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const float qv = qs[bb][p];
-        acc[bb][0] = fmaf(qv, w0, acc[bb][0]);
-        acc[bb][1] = fmaf(qv, w1, acc[bb][1]);
-        acc[bb][2] = fmaf(qv, w2, acc[bb][2]);
-        acc[bb][3] = fmaf(qv, w3, acc[bb][3]);
-      }
-    }
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-      if (b0 + bb < B)
-        *reinterpret_cast<float4*>(u + (size_t)(b0 + bb) * (size_t)H + h) =
-            make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+    for (int bb = 0; bb < 4; ++bb)
+      v[bb] = (b0 + bb < B) ? q[(size_t)(b0 + bb) * (size_t)P + p] : 0.0f;
+    qs[p] = make_float4(v[0], v[1], v[2], v[3]);
   }
+  __syncthreads();
+  float acc[4][8];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0f;
+  if (h < H) {
+#pragma unroll 4
+    for (int p = wave; p < P; p += 4) {
+      const uint4 v = load_piece<false>(w + (size_t)p * (size_t)H + h);
+      const float wf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+      const float4 qv = qs[p];
+      const float qb[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(qb[bb], wf[e], acc[bb][e]);
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave][bb][e][lane] = acc[bb][e];
+  __syncthreads();
+  // wave w now finishes question b0 + w
+  const long long b = b0 + wave;
+  if (b >= B || h >= H) return;
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    r[e] = ((part[0][wave][e][lane] + part[1][wave][e][lane]) + part[2][wave][e][lane]) +
+           part[3][wave][e][lane];
+  float4* dst = reinterpret_cast<float4*>(u + (size_t)b * (size_t)H + h);
+  dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+  dst[1] = make_float4(r[4], r[5], r[6], r[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -215,9 +246,8 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
 // owns rows 64*(w % 4) .. +64 (two 32-row MFMA tiles) and columns
 // 32*TN*(w / 4) .. +32*TN (TN 32-column tiles), so P = 64 * TN <= 256.
 // The hidden dimension is staged through LDS 64 bf16 at a time (rows padded
-// by 16 bytes against bank conflicts).
+// by 16 bytes against bank conflicts), double-buffered (2 x 72 KiB).
 constexpr int kChunk = 64;
-constexpr int kMaxGridY = 16384;  // question blocks beyond this are strided
 constexpr int kRowStride = kChunk + 8;  // bf16 per LDS row
 
 template <int TN, bool NT>
@@ -225,8 +255,8 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
                                                      const uint16_t* __restrict__ xc,
                                                      const uint16_t* __restrict__ wc,
                                                      const float* __restrict__ qp) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[256 * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[256 * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][256 * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][256 * kRowStride];
   __shared__ Lds s;
   constexpr int P = 64 * TN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -241,22 +271,40 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
     const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
-    for (int h0 = 0; h0 < H; h0 += kChunk) {
-      // Stage 256 rows x 64 of X (zero past K) and P rows x 64 of Wc.
+    // Double-buffered staging: while the matrix cores work on chunk c from
+    // one LDS buffer, the loads of chunk c+1 are in flight to registers; they
+    // land in the other buffer before the one barrier per chunk.
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    uint4 px[4], pw[4];
+    auto fetch = [&](int c) {
+      const int h0 = c * kChunk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int id = tid + 512 * i;
         const int row = id >> 3, c8 = id & 7;
         const int hh = h0 + 8 * c8;
         const bool in_h = hh < H;
-        const uint4 xv = (row < K && in_h) ? load_piece<NT>(Xb + (size_t)row * (size_t)H + hh)
-                                           : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&sX[row * kRowStride + 8 * c8]) = xv;
-        const uint4 wv = (row < P && in_h) ? load_piece<false>(wc + (size_t)row * (size_t)H + hh)
-                                           : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&sW[row * kRowStride + 8 * c8]) = wv;
+        px[i] = (row < K && in_h) ? load_piece<NT>(Xb + (size_t)row * (size_t)H + hh)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+        pw[i] = (row < P && in_h) ? load_piece<false>(wc + (size_t)row * (size_t)H + hh)
+                                  : make_uint4(0u, 0u, 0u, 0u);
       }
-      __syncthreads();
+    };
+    auto deposit = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int id = tid + 512 * i;
+        const int row = id >> 3, c8 = id & 7;
+        *reinterpret_cast<uint4*>(&sX[buf][row * kRowStride + 8 * c8]) = px[i];
+        *reinterpret_cast<uint4*>(&sW[buf][row * kRowStride + 8 * c8]) = pw[i];
+      }
+    };
+    fetch(0);
+    deposit(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nchunks) fetch(c + 1);
 #pragma unroll
       for (int ks = 0; ks < kChunk / 16; ++ks) {
         // Lane l feeds row/column l % 32 and hidden elements 8*(l/32) .. +8
@@ -266,11 +314,11 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           af[rb] = *reinterpret_cast<const bf16x8_t*>(
-              &sX[(64 * wr + 32 * rb + (lane & 31)) * kRowStride + kofs]);
+              &sX[buf][(64 * wr + 32 * rb + (lane & 31)) * kRowStride + kofs]);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
           bfr[tn] = *reinterpret_cast<const bf16x8_t*>(
-              &sW[(32 * TN * wcb + 32 * tn + (lane & 31)) * kRowStride + kofs]);
+              &sW[buf][(32 * TN * wcb + 32 * tn + (lane & 31)) * kRowStride + kofs]);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -278,6 +326,7 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
             acc[rb][tn] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[tn], acc[rb][tn], 0, 0, 0);
       }
+      if (c + 1 < nchunks) deposit(buf ^ 1);
       __syncthreads();
     }
     // Epilogue. Accumulator e of tile (rb, tn) in lane l holds C'[row][col]
@@ -405,11 +454,12 @@ int bf16_nv_for(int Hc) {
 }
 
 hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
-  // q' = Wq x_q for every question.
-  hipLaunchKernelGGL(proj_query,
-                     dim3((unsigned)((p.P + kWave - 1) / kWave),
-                          (unsigned)std::min((p.B + 3) / 4, kMaxGridY)),
-                     dim3(256), 0, stream, p.xq, p.wq, p.qp, p.B, p.Hq, p.P);
+  // q' = Wq x_q for every question: one wave per 8 x 8 tile.
+  {
+    const long long waves = (long long)((p.B + 7) / 8) * ((p.P + 7) / 8);
+    hipLaunchKernelGGL(proj_query, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, p.xq,
+                       p.wq, p.qp, p.B, p.Hq, p.P);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   KernelArgs a{};
@@ -422,10 +472,13 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.zscale = p.zscale;
   a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
-  // u = Wc^T q', then one bandwidth-bound pass over the candidates.
-  hipLaunchKernelGGL(fold_query,
-                     dim3((unsigned)((p.Hc + 1023) / 1024), (unsigned)std::min((p.B + 7) / 8, kMaxGridY)),
-                     dim3(256), 0, stream, p.qp, p.wc, p.u, p.B, p.Hc, p.P);
+  // u = Wc^T q' (one workgroup per 4 questions x 512 h), then one
+  // bandwidth-bound pass over the candidates.
+  {
+    const long long groups = (long long)((p.B + 3) / 4) * ((p.Hc + 511) / 512);
+    hipLaunchKernelGGL(fold_query, dim3((unsigned)groups), dim3(256), 0, stream, p.qp, p.wc, p.u,
+                       p.B, p.Hc, p.P);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nv = bf16_nv_for(p.Hc);
