@@ -39,7 +39,7 @@ sys.path.insert(0, str(ROOT))
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = ROOT / "candidate_scoring_amd" / "csrc" / "cs_kernels.hip"
+KERNEL_SOURCES = [ROOT / "candidate_scoring_amd" / "csrc" / n for n in ("cs_kernels.hip", "cs_device.h")]
 TRAFFIC_PROFILE = ROOT / "profiles" / "fused_regq_kev_batch1024_255x2560_traffic.md"
 LATENCY_CONFIGS = ["clm_cos_5x512", "clm_cos_255x512", "clm_cos_batch8_255x512",
                    "kev_dot_255x2560"]
@@ -50,9 +50,10 @@ def log(msg):
 
 
 def source_sha256() -> str:
-    """sha256 of the kernel source with comments and whitespace removed, so
-    that only code changes count as a changed kernel."""
-    text = KERNEL_SOURCE.read_text()
+    """sha256 of the scoring kernels' source (kernel file and shared device
+    header) with comments and whitespace removed, so that only code changes
+    count as a changed kernel."""
+    text = "\n".join(f.read_text() for f in KERNEL_SOURCES)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
