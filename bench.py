@@ -60,6 +60,22 @@ def source_sha256() -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+OCCUPANCY_PROFILE = ROOT / "profiles" / "occupancy_kernels.md"
+
+
+def committed_occupancy():
+    """OccupancyPercent of the headline kernel from the committed counter
+    profile, or None when missing or taken on different kernel code."""
+    if not OCCUPANCY_PROFILE.exists():
+        return None
+    text = OCCUPANCY_PROFILE.read_text()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_occ = re.search(r"occupancy_percent_headline:\s*([0-9.]+)", text)
+    if not m_sha or not m_occ or m_sha.group(1) != source_sha256():
+        return None
+    return float(m_occ.group(1))
+
+
 def committed_traffic():
     """HBM bytes per launch from the committed counter profile, or None when
     it is missing or was taken on a different kernel source."""
@@ -434,6 +450,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "occupancy_percent": committed_occupancy(),
                      "kernel": "fused_regq<dot, nv=10, rows=2, full, nontemporal>",
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
     }
