@@ -17,6 +17,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "cs_launch.h"
@@ -89,6 +90,29 @@ bool is_device_pointer(const void* p) {
     return false;
   }
   return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+// Compute units of the current device, queried once per device (0 when the
+// query fails: the launchers then fall back to one workgroup per question).
+int device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 int plan_groups(int B, int K, int D) {
@@ -296,6 +320,7 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.zscale = (float)((double)scale / (double)temperature);
   p.cosine = sim == CS_SIM_COSINE;
   p.nt = 2.0 * (double)B * (double)K * (double)Hc >= kStreamBytes ? 1 : 0;
+  p.compute_units = device_compute_units();
   const hipError_t err = cs::launch_projected(p, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;

@@ -57,6 +57,7 @@ struct ProjArgs {
   float zscale;        // scale / temperature
   int cosine;
   int nt;              // stream the candidate rows non-temporally
+  int compute_units;   // compute units of the current device (persistent grids)
 };
 // 16-byte pieces per lane of the bf16 dot kernel for Hc (Hc % 8 == 0); 0 if
 // Hc is too large.

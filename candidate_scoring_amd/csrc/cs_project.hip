@@ -240,6 +240,66 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
   }
 }
 
+// Epilogue of the cosine tile: each row of C' reduced to c'.q' and |c'|^2,
+// the two feature halves added in a fixed order into the softmax's LDS
+// slots, then the softmax itself. Called by every thread of the workgroup.
+template <int TN>
+__device__ __forceinline__ void cos_epilogue(Lds& s, const KernelArgs& a,
+                                             const float* __restrict__ qp,
+                                             const f32x16_t (&acc)[2][TN], int b, int K,
+                                             int lane, int wave, int wr, int wcb) {
+  constexpr int P = 64 * TN;
+  // Epilogue. Accumulator e of tile (rb, tn) in lane l holds C'[row][col]
+  // with row = 64*wr + 32*rb + 8*(e/4) + 4*(l/32) + e%4 and
+  // col = 32*TN*wcb + 32*tn + l%32.
+  float qv[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    qv[tn] = qp[(size_t)b * P + 32 * TN * wcb + 32 * tn + (lane & 31)];
+  float dv[32], ev[32];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float d = 0.0f, q2 = 0.0f;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const float c = acc[rb][tn][e];
+        d = fmaf(c, qv[tn], d);
+        q2 = fmaf(c, c, q2);
+      }
+      dv[16 * rb + e] = d;
+      ev[16 * rb + e] = q2;
+    }
+  const float dsum = halfwave_reduce_transposed<32>(dv, lane, OpSum());
+  const float esum = halfwave_reduce_transposed<32>(ev, lane, OpSum());
+  const int v = lane & 31, rb = v >> 4, e = v & 15;
+  const int row = 64 * wr + 32 * rb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  // The two column halves of a row are added in a fixed order.
+  if (wcb == 0) {
+    s.dot[row] = dsum;
+    s.ss[row] = esum;
+  }
+  __syncthreads();
+  if (wcb == 1) {
+    s.dot[row] += dsum;
+    s.ss[row] += esum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float qq = 0.0f;
+    for (int p = lane; p < P; p += kWave) {
+      const float x = qp[(size_t)b * P + p];
+      qq = fmaf(x, x, qq);
+    }
+    qq = wave_allreduce(qq, lane, OpSum());
+    const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
+    const Question qn{(size_t)b * (size_t)K, K};
+    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane);
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Cosine: per question, C' = X Wc^T on the matrix cores, fused with the
 // similarity and the softmax. One workgroup of 8 waves per question; wave w
@@ -329,55 +389,317 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
       if (c + 1 < nchunks) deposit(buf ^ 1);
       __syncthreads();
     }
-    // Epilogue. Accumulator e of tile (rb, tn) in lane l holds C'[row][col]
-    // with row = 64*wr + 32*rb + 8*(e/4) + 4*(l/32) + e%4 and
-    // col = 32*TN*wcb + 32*tn + l%32.
-    float qv[TN];
+    cos_epilogue<TN>(s, a, qp, acc, b, K, lane, wave, wr, wcb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same cosine tile with asynchronous staging (Hc % 64 == 0): the hidden
+// dimension moves through two LDS stages of 64 bf16 per row, filled by
+// global_load_lds_dwordx4 (no staging registers): one chunk is in flight
+// while the matrix cores work on the other. Rows of 128 bytes make every
+// request to L2 a whole cache line (half-line requests held the per-CU
+// request queue to half the bytes in flight). The DMA writes each wave's 64
+// lanes to 1 KiB of consecutive LDS, i.e. 8 rows; to keep the fragment reads
+// free of bank conflicts, the lane that fills 16-byte position p of row r
+// fetches piece p ^ f(r) of that row (an XOR swizzle instead of padding),
+// and readers undo it.
+//
+// The fragment reads are inline assembly that the compiler does not track, so
+// it adds no wait for the DMAs in flight; the ring's explicit vmcnt waits and
+// barriers order every read after the DMA that fills its stage.
+constexpr int kAChunk = 64;                        // bf16 per row per stage
+constexpr int kAStages = 2;                        // 128 KiB of LDS
+constexpr int kARowBytes = 2 * kAChunk;            // 128
+constexpr int kAPieces = kARowBytes / 16;          // 8 pieces of 16 bytes per row
+constexpr int kARowsPerLoad = 1024 / kARowBytes;   // 8 rows per DMA instruction
+constexpr int kATileBytes = 256 * kARowBytes;      // X or W tile of one stage: 32 KiB
+constexpr int kAKSteps = kAChunk / 16;             // 4 MFMA k-steps per chunk
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs[kAStages][kATileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ws[kAStages][kATileBytes];
+__shared__ __attribute__((aligned(1024))) float g_qp[256];  // q' of the current question
+
+// X tile (W == false) or W tile (W == true) of stage S.
+template <int S, bool W>
+__device__ __forceinline__ uint8_t* stage_tile() {
+  static_assert(S >= 0 && S < kAStages, "stage index");
+  return W ? g_ws[S] : g_xs[S];
+}
+
+typedef __attribute__((address_space(1))) const void* global_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Physical 16-byte position of logical piece `piece` of row `row`. The
+// mapping depends on row % 16 only (so the 32-row blocks a lane reads share
+// it), and any 16 consecutive rows reading the same logical piece hit
+// distinct banks.
+__device__ __forceinline__ int swizzled_piece(int row, int piece) {
+  return piece ^ ((row & 7) ^ ((row >> 3) & 1));
+}
+
+// s_waitcnt with only the vector-memory count limited to n (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the stage ring: this wave's LDS reads are complete
+// (lgkmcnt 0) before it arrives, and no memory access is moved across it by
+// the compiler. Unlike __syncthreads it does not wait for the DMA loads still
+// in flight; the callers wait for exactly the ones they need.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// DMA of hidden chunk c into stage S: this wave fills rows 32*wave .. +32 of
+// the X tile and of the W tile. X rows past K repeat row K-1 and W rows past
+// P repeat row P-1; those rows are never read. (The helpers take plain
+// pointers: restrict-qualified parameters of an inlined function would give
+// every call site alias scopes of its own.)
+template <int S, bool NT>
+__device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* wc, int c, int K,
+                                           int P, int H, int wave, int lane) {
+  const int h0 = c * kAChunk;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      qv[tn] = qp[(size_t)b * P + 32 * TN * wcb + 32 * tn + (lane & 31)];
-    float dv[32], ev[32];
+  for (int j = 0; j < 32 / kARowsPerLoad; ++j) {
+    const int r0 = 32 * wave + kARowsPerLoad * j;
+    const int row = r0 + lane / kAPieces;
+    const int piece = swizzled_piece(row, lane % kAPieces);
+    const uint16_t* src = Xb + (size_t)min(row, K - 1) * (size_t)H + h0 + 8 * piece;
+    __builtin_amdgcn_global_load_lds((global_ptr_t)src,
+                                     (lds_ptr_t)(stage_tile<S, false>() + r0 * kARowBytes), 16, 0,
+                                     NT ? 2 : 0);
+    const uint16_t* wsrc = wc + (size_t)min(row, P - 1) * (size_t)H + h0 + 8 * piece;
+    __builtin_amdgcn_global_load_lds((global_ptr_t)wsrc,
+                                     (lds_ptr_t)(stage_tile<S, true>() + r0 * kARowBytes), 16, 0,
+                                     0);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// One 16-byte fragment read from LDS at byte address addr + OFF. Written as
+// inline assembly so that the compiler, which cannot always tell which DMA
+// stage a read depends on, does not add a wait for every DMA in flight; the
+// ring's own vmcnt waits and barriers order the reads instead. The result is
+// not ready until lds_fragments_ready().
+template <int OFF>
+__device__ __forceinline__ void lds_fragment(bf16x8_t& f, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+
+// Waits for every fragment read issued so far and makes each fragment a
+// result of the wait, so nothing that uses one can be scheduled before it.
+template <int TN>
+__device__ __forceinline__ void lds_fragments_ready(bf16x8_t (&af)[2], bf16x8_t (&bfr)[TN]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) asm volatile("" : "+v"(af[rb]));
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(bfr[tn]));
+}
+
+// Per-lane byte offsets of the two 16-wide steps of a chunk inside an X tile
+// (rows 64*wr + lane%32, +32) and a W tile (rows 32*TN*wcb + lane%32, +32,
+// ...). The swizzle depends on row % 16 only, so the 32-row blocks of one
+// lane share it and sit 2 KiB apart.
+struct StageOffsets {
+  uint32_t x[kAKSteps], w[kAKSteps];
+};
+
+template <int TN>
+__device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int wcb) {
+  StageOffsets o;
+  const int rx = 64 * wr + (lane & 31), rw = 32 * TN * wcb + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < kAKSteps; ++ks) {
+    const int piece = 2 * ks + (lane >> 5);
+    o.x[ks] = (uint32_t)(rx * kARowBytes + 16 * swizzled_piece(rx, piece));
+    o.w[ks] = (uint32_t)(rw * kARowBytes + 16 * swizzled_piece(rw, piece));
+  }
+  return o;
+}
+
+template <int S, int TN>
+__device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[2][TN], const StageOffsets& o) {
+  const uint32_t xs = lds_address(stage_tile<S, false>());
+  const uint32_t ws = lds_address(stage_tile<S, true>());
+#pragma unroll
+  for (int ks = 0; ks < kAKSteps; ++ks) {
+    bf16x8_t af[2], bfr[TN];
+    const uint32_t xa = xs + o.x[ks], wa = ws + o.w[ks];
+    lds_fragment<0>(af[0], xa);
+    lds_fragment<32 * kARowBytes>(af[1], xa);
+    lds_fragment<0>(bfr[0], wa);
+    if constexpr (TN > 1) lds_fragment<32 * kARowBytes>(bfr[TN > 1 ? 1 : 0], wa);
+    if constexpr (TN > 2) lds_fragment<64 * kARowBytes>(bfr[TN > 2 ? 2 : 0], wa);
+    if constexpr (TN > 3) lds_fragment<96 * kARowBytes>(bfr[TN > 3 ? 3 : 0], wa);
+    lds_fragments_ready<TN>(af, bfr);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float d = 0.0f, q2 = 0.0f;
+      for (int tn = 0; tn < TN; ++tn)
+        acc[rb][tn] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[tn], acc[rb][tn], 0, 0, 0);
+  }
+}
+
+// One chunk of the ring: wait until chunk c (stage S) of the current question
+// has landed for every wave, refill the stage freed by chunk c-1 with chunk
+// c+1, multiply chunk c. Chunk c+1 may be the first of the next question of
+// this workgroup (Xn; null when there is none or when questions do not carry
+// the ring). The step with c < 0 only fills (the start of the ring).
+template <int S, int TN, bool NT>
+__device__ __forceinline__ void stage_step(f32x16_t (&acc)[2][TN], const StageOffsets& o,
+                                           const uint16_t* Xb, const uint16_t* Xn,
+                                           const uint16_t* wc, int c, int nchunks, int K, int H,
+                                           int wave, int lane) {
+  if (c >= nchunks) return;
+  if (c >= 0) {
+    // With two stages the only chunk in flight is c itself (issued at the
+    // start of the previous step); stores issued since only add to the wait.
+    wait_vmcnt<0>();
+    stage_barrier();
+  }
+  int next = c + kAStages - 1;
+  const uint16_t* src = Xb;
+  if (next >= nchunks) {
+    next -= nchunks;
+    src = Xn;
+  }
+  if (next >= 0 && src != nullptr)
+    stage_fill<(S + kAStages - 1) % kAStages, NT>(src, wc, next, K, 64 * TN, H, wave, lane);
+  if (c >= 0) stage_mfma<S, TN>(acc, o);
+}
+
+// DMA of the current question's q' (P floats) into g_qp by one wave: lane l
+// brings floats 4l .. 4l+3 (lanes past P repeat the last four; unused).
+__device__ __forceinline__ void qp_fill(const float* qrow, int P, int lane) {
+  const float* src = qrow + min(4 * lane, P - 4);
+  __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)g_qp, 16, 0, 0);
+}
+
+// One float read from LDS byte address addr, untracked by the compiler like
+// lds_fragment(); ready after lds_values_ready().
+__device__ __forceinline__ void lds_value(float& v, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_values_ready(float (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const float c = acc[rb][tn][e];
-          d = fmaf(c, qv[tn], d);
-          q2 = fmaf(c, c, q2);
-        }
-        dv[16 * rb + e] = d;
-        ev[16 * rb + e] = q2;
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// Epilogue of the ring kernel: as cos_epilogue, with q' taken from g_qp
+// (brought in by DMA when the question started, so nothing here waits on the
+// vector-memory counter) and barriers that do not wait for the next
+// question's DMAs already in flight. The ring's last wait covered the q' DMA,
+// which wave 0 issued before the question's later chunks.
+template <int TN>
+__device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
+                                                  const f32x16_t (&acc)[2][TN], int b, int K,
+                                                  int lane, int wave, int wr, int wcb) {
+  const uint32_t qbase = lds_address(reinterpret_cast<const uint8_t*>(g_qp));
+  float qv[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    lds_value(qv[tn], qbase + 4u * (uint32_t)(32 * TN * wcb + 32 * tn + (lane & 31)));
+  lds_values_ready<TN>(qv);
+  float dv[32], ev[32];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float d = 0.0f, q2 = 0.0f;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const float c = acc[rb][tn][e];
+        d = fmaf(c, qv[tn], d);
+        q2 = fmaf(c, c, q2);
       }
-    const float dsum = halfwave_reduce_transposed<32>(dv, lane, OpSum());
-    const float esum = halfwave_reduce_transposed<32>(ev, lane, OpSum());
-    const int v = lane & 31, rb = v >> 4, e = v & 15;
-    const int row = 64 * wr + 32 * rb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    // The two column halves of a row are added in a fixed order.
-    if (wcb == 0) {
-      s.dot[row] = dsum;
-      s.ss[row] = esum;
+      dv[16 * rb + e] = d;
+      ev[16 * rb + e] = q2;
     }
-    __syncthreads();
-    if (wcb == 1) {
-      s.dot[row] += dsum;
-      s.ss[row] += esum;
+  const float dsum = halfwave_reduce_transposed<32>(dv, lane, OpSum());
+  const float esum = halfwave_reduce_transposed<32>(ev, lane, OpSum());
+  const int v = lane & 31, rb = v >> 4, e = v & 15;
+  const int row = 64 * wr + 32 * rb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  // The two column halves of a row are added in a fixed order.
+  if (wcb == 0) {
+    s.dot[row] = dsum;
+    s.ss[row] = esum;
+  }
+  stage_barrier();
+  if (wcb == 1) {
+    s.dot[row] += dsum;
+    s.ss[row] += esum;
+  }
+  stage_barrier();
+  if (wave == 0) {
+    float qpv[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) lds_value(qpv[i], qbase + 4u * (uint32_t)(lane + kWave * i));
+    lds_values_ready<TN>(qpv);
+    float qq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) qq = fmaf(qpv[i], qpv[i], qq);
+    qq = wave_allreduce(qq, lane, OpSum());
+    const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
+    const Question qn{(size_t)b * (size_t)K, K};
+    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane);
+  }
+  // No barrier here: wave 0 reaches the next question's first ring barrier
+  // only after the softmax, and s.dot / s.ss are written again only after it.
+}
+
+// A workgroup takes questions blockIdx.x, blockIdx.x + gridDim.x, ... and,
+// when the chunk count is a multiple of the stage count, keeps the ring
+// running across them: the first three chunks of the next question are in
+// flight during the last steps and the epilogue of the current one.
+template <int TN, bool NT>
+__global__ __launch_bounds__(512) void proj_cos_mfma_async(KernelArgs a,
+                                                           const uint16_t* __restrict__ xc,
+                                                           const uint16_t* __restrict__ wc,
+                                                           const float* __restrict__ qp) {
+  static_assert(kAStages == 2, "the chunk loop is unrolled by the stage count");
+  __shared__ Lds s;
+  constexpr int P = 64 * TN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wr = wave & 3, wcb = wave >> 2;
+  const int H = a.D, K = a.K;
+  const int nchunks = H / kAChunk;
+  const bool carry = nchunks % kAStages == 0;
+  const int stride = (int)gridDim.x;
+  const StageOffsets o = stage_offsets<TN>(lane, wr, wcb);
+  for (int b = blockIdx.x; b < a.B; b += stride) {
+    const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
+    const uint16_t* Xn =
+        (carry && b + stride < a.B) ? xc + (size_t)(b + stride) * (size_t)K * (size_t)H : nullptr;
+    if (wave == 0) qp_fill(qp + (size_t)b * P, P, lane);
+    f32x16_t acc[2][TN];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
+    if (!carry || b == (int)blockIdx.x)
+      stage_step<1, TN, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane);
+    for (int c = 0; c < nchunks; c += kAStages) {
+      stage_step<0, TN, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane);
+      stage_step<1, TN, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane);
     }
-    __syncthreads();
-    if (wave == 0) {
-      float qq = 0.0f;
-      for (int p = lane; p < P; p += kWave) {
-        const float x = qp[(size_t)b * P + p];
-        qq = fmaf(x, x, qq);
-      }
-      qq = wave_allreduce(qq, lane, OpSum());
-      const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
-      const Question qn{(size_t)b * (size_t)K, K};
-      slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane);
-    }
-    __syncthreads();
+    cos_epilogue_ring<TN>(s, a, acc, b, K, lane, wave, wr, wcb);
   }
 }
 
@@ -414,28 +736,28 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
   }
 }
 
+template <int TN, bool NT>
+void launch_cos_tile(const KernelArgs& a, const ProjArgs& p, unsigned grid, hipStream_t stream) {
+  if (p.Hc % kAChunk == 0)
+    // One resident workgroup per compute unit (its LDS allows no more), each
+    // working through its share of the questions.
+    hipLaunchKernelGGL((proj_cos_mfma_async<TN, NT>),
+                       dim3(p.compute_units > 0 ? std::min(grid, (unsigned)p.compute_units) : grid),
+                       dim3(512), 0, stream, a, p.xc, p.wc, p.qp);
+  else
+    hipLaunchKernelGGL((proj_cos_mfma<TN, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
+                       p.qp);
+}
+
 template <bool NT>
 hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t stream) {
   const unsigned grid = (unsigned)std::min(p.B, 1 << 20);
   switch (p.P / 64) {
-    case 1:
-      hipLaunchKernelGGL((proj_cos_mfma<1, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
-                         p.qp);
-      break;
-    case 2:
-      hipLaunchKernelGGL((proj_cos_mfma<2, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
-                         p.qp);
-      break;
-    case 3:
-      hipLaunchKernelGGL((proj_cos_mfma<3, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
-                         p.qp);
-      break;
-    case 4:
-      hipLaunchKernelGGL((proj_cos_mfma<4, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
-                         p.qp);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 1: launch_cos_tile<1, NT>(a, p, grid, stream); break;
+    case 2: launch_cos_tile<2, NT>(a, p, grid, stream); break;
+    case 3: launch_cos_tile<3, NT>(a, p, grid, stream); break;
+    case 4: launch_cos_tile<4, NT>(a, p, grid, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -71,6 +71,12 @@ def dev(cs):
     (2, 64, 128, 1000, 192, "cosine"),
     (5, 5, 64, 24, 64, "cosine"),
     (2, 1, 64, 64, 64, "cosine"),
+    (2, 130, 64, 32, 128, "cosine"),       # hidden below one 64-wide chunk
+    (3, 255, 64, 96, 192, "cosine"),       # hidden not a multiple of 64: staged in registers
+    (2, 255, 64, 64, 256, "cosine"),       # one chunk of the DMA ring
+    (3, 255, 64, 192, 192, "cosine"),      # three chunks: the ring restarts per question
+    (2, 200, 64, 320, 256, "cosine"),      # five chunks
+    (3, 17, 64, 2048, 64, "cosine"),
     (3, 77, 520, 1000, 96, "dot"),
     (2, 255, 8, 8, 8, "dot"),
     (2, 100, 136, 4096, 256, "dot"),
@@ -79,6 +85,18 @@ def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
     note(f"case projected B={B} K={K} Hq={Hq} Hc={Hc} P={P} {sim}")
     check(run(cs, w, dev), want(orc, w), f"B={B} K={K} Hc={Hc} P={P} {sim}")
+
+
+@pytest.mark.parametrize("B,K,Hc,P", [
+    (600, 33, 256, 128),   # even chunk count: the ring runs across questions
+    (300, 40, 192, 64),    # three chunks: the ring restarts for every question
+])
+def test_projected_cosine_many_questions(cs, orc, dev, B, K, Hc, P):
+    """More questions than compute units, so a workgroup of the cosine kernel
+    takes several questions in turn; every question is checked."""
+    w = workloads.projected_inputs(97 + B, B, K, 64, Hc, P, "cosine")
+    note(f"case projected many questions B={B} K={K} Hc={Hc} P={P}")
+    check(run(cs, w, dev), want(orc, w), f"B={B} K={K} Hc={Hc} P={P} cosine")
 
 
 def test_projected_temperature(cs, orc, dev):
