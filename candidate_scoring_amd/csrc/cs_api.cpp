@@ -273,9 +273,20 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   return CS_OK;
 }
 
+// Projected-query workspace: q' [B][P] fp32; for dot also u [B][Hc] fp32
+// and the three-part bf16 split of q' [B][3 * P16] (P16 = P rounded up to 16).
+size_t projected_qp_bytes(int B, int P) {
+  return align_up(sizeof(float) * (size_t)B * (size_t)P, 256);
+}
+size_t projected_u_bytes(int B, int Hc) {
+  return align_up(sizeof(float) * (size_t)B * (size_t)Hc, 256);
+}
 size_t projected_workspace(int B, int Hc, int P, int sim) {
-  size_t bytes = align_up(sizeof(float) * (size_t)B * (size_t)P, 256);
-  if (sim == CS_SIM_DOT) bytes += sizeof(float) * (size_t)B * (size_t)Hc;
+  size_t bytes = projected_qp_bytes(B, P);
+  if (sim == CS_SIM_DOT) {
+    const size_t p16 = (size_t)(P + 15) / 16 * 16;
+    bytes += projected_u_bytes(B, Hc) + sizeof(uint16_t) * (size_t)B * 3 * p16;
+  }
   return bytes;
 }
 
@@ -310,8 +321,9 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.wc = wc;
   p.out = out;
   p.qp = static_cast<float*>(ws);
-  p.u = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                 align_up(sizeof(float) * (size_t)B * (size_t)P, 256));
+  p.u = reinterpret_cast<float*>(static_cast<char*>(ws) + projected_qp_bytes(B, P));
+  p.parts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + projected_qp_bytes(B, P) +
+                                        projected_u_bytes(B, Hc));
   p.B = B;
   p.K = K;
   p.Hq = Hq;

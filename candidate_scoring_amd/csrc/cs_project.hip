@@ -10,8 +10,8 @@
 //
 // Two shapes of the same computation:
 //  * dot (Kev): c'_k . q' = x_k . (Wc^T q'), so the candidate head folds into
-//    the query. proj_query makes q' [B][P], fold_query makes u = Wc^T q'
-//    [B][Hc], and fused_bf16_dot streams the bf16 candidate rows once against
+//    the query. proj_query_mfma makes q' [B][P], fold_query_mfma makes
+//    u = Wc^T q' [B][Hc], and fused_bf16_dot streams the bf16 candidate rows once against
 //    u, with the same in-workgroup softmax as the plain scoring kernels. The
 //    candidate side stays a bandwidth-bound pass; no candidate is projected.
 //  * cosine (CLM): the norm |Wc x_k| needs the projected rows, a dense
@@ -75,109 +75,274 @@ __device__ __forceinline__ float halfwave_reduce_transposed(float (&v)[V], int l
 }
 
 // ---------------------------------------------------------------------------
-// q'[b][p] = sum_h x[b][h] * w[p][h]  (x [B][H], w [P][H], bf16; H % 8 == 0).
-// A wave computes an 8-question x 8-output tile: lane l reads 16-byte pieces
-// 8l, 8l + 512, ... of the 8 query rows and the 8 weight rows (every load a
-// contiguous 1 KiB across the wave), accumulates the 64 partial dots, and one
-// transposed 64-value reduction leaves output (l / 8, l % 8) in lane l.
-__global__ __launch_bounds__(256) void proj_query(const uint16_t* __restrict__ x,
-                                                  const uint16_t* __restrict__ w,
-                                                  float* __restrict__ q, int B, int H, int P) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const long long wid = (long long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  const int ptiles = (P + 7) / 8;
-  const long long b0 = (wid / ptiles) * 8;
-  const int p0 = (int)(wid % ptiles) * 8;
-  if (b0 >= B) return;  // uniform across the wave
-  float acc[64];
+// LDS staging helpers shared by the matrix-core kernels.
+
+typedef __attribute__((address_space(1))) const void* global_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Physical 16-byte position of logical piece `piece` of a 128-byte LDS row
+// `row`. The mapping depends on row % 16 only (so 32-row blocks share it),
+// and any 16 consecutive rows reading the same logical piece hit distinct
+// banks.
+__device__ __forceinline__ int swizzled_piece(int row, int piece) {
+  return piece ^ ((row & 7) ^ ((row >> 3) & 1));
+}
+
+// s_waitcnt with only the vector-memory count limited to n (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+
+// One 16-byte fragment read from LDS at byte address addr + OFF. Written as
+// inline assembly so that the compiler, which cannot always tell which DMA
+// a read depends on, does not add a wait for every DMA in flight; the
+// kernels' own vmcnt waits and barriers order the reads instead. The result
+// is not ready until an lgkmcnt(0) wait (lds_fragments_ready()).
+template <int OFF>
+__device__ __forceinline__ void lds_fragment(bf16x8_t& f, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+
+// x = hi + mid + lo exactly (bar underflow): each part is the bf16 rounding
+// of what the parts before it leave over; both residues are exact in fp32
+// and the last one has at most 8 significant bits. The parts are returned as
+// fp32 values that bf16 represents exactly.
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+__device__ __forceinline__ float3 split3(float x) {
+  const float hi = bf16_round(x);
+  const float r1 = x - hi;
+  const float mid = bf16_round(r1);
+  return make_float3(hi, mid, bf16_round(r1 - mid));
+}
+// Bits of a float that bf16 represents exactly.
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return (uint16_t)(__float_as_uint(x) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// q'[b][p] = sum_h x[b][h] * w[p][h]  (x [B][H], w [P][H], bf16; H % 8 == 0)
+// on the matrix cores. One workgroup of 16 waves per 32 x 32 tile of q'; the
+// hidden sum is split over the waves in 64-wide blocks (wave w takes blocks
+// w, w+16, ...), and a wave issues the loads of two blocks before
+// its first multiply, so the tile's operands are in flight at once. Both
+// operands come straight from global memory: in a block, lane l takes row
+// l % 32 and the 32 consecutive hidden elements 32*(l/32) .. +32, four
+// 16-byte pieces, and piece j of both operands feeds the j-th
+// v_mfma_f32_32x32x16_bf16 -- the same hidden indices pair up on both sides,
+// which is all a contraction needs. bf16 products are exact in fp32; the 16
+// partial tiles are added in wave order through LDS.
+constexpr int kPqWaves = 16;
+constexpr int kPqDepth = 2;  // blocks in flight per wave
+
+__global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ q,
+    uint16_t* __restrict__ parts, int B, int H, int P) {
+  __shared__ float part[kPqWaves][16][kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int ptiles = (P + 31) / 32;
+  const long long b0 = (long long)(blockIdx.x / ptiles) * 32;
+  const int p0 = (int)(blockIdx.x % ptiles) * 32;
+  const int r = lane & 31, half = lane >> 5;
+  const uint16_t* xr = x + (size_t)min(b0 + r, (long long)B - 1) * (size_t)H;
+  const uint16_t* wr = w + (size_t)min(p0 + r, P - 1) * (size_t)H;
+  f32x16_t acc;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.0f;
-  for (int h = 8 * lane; h < H; h += 8 * kWave) {
-    float wf[8][8];
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  const int nblk = (H + 63) / 64;
+  for (int kb0 = wave; kb0 < nblk; kb0 += kPqDepth * kPqWaves) {
+    bf16x8_t av[kPqDepth][4], wv[kPqDepth][4];
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      const uint4 v = (p0 + pp < P) ? load_piece<false>(w + (size_t)(p0 + pp) * (size_t)H + h)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-      wf[pp][0] = bf_lo(v.x); wf[pp][1] = bf_hi(v.x); wf[pp][2] = bf_lo(v.y); wf[pp][3] = bf_hi(v.y);
-      wf[pp][4] = bf_lo(v.z); wf[pp][5] = bf_hi(v.z); wf[pp][6] = bf_lo(v.w); wf[pp][7] = bf_hi(v.w);
+    for (int d = 0; d < kPqDepth; ++d) {
+      const int kb = kb0 + d * kPqWaves;
+      const int k = 64 * kb + 32 * half;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kb < nblk && k + 8 * j < H) {
+          av[d][j] = *reinterpret_cast<const bf16x8_t*>(xr + k + 8 * j);
+          wv[d][j] = *reinterpret_cast<const bf16x8_t*>(wr + k + 8 * j);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            av[d][j][e] = (__bf16)0.0f;
+            wv[d][j][e] = (__bf16)0.0f;
+          }
+        }
+      }
     }
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const uint4 v = (b0 + bb < B) ? load_piece<false>(x + (size_t)(b0 + bb) * (size_t)H + h)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-      const float xf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+    for (int d = 0; d < kPqDepth; ++d)
 #pragma unroll
-      for (int pp = 0; pp < 8; ++pp)
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[d][j], wv[d][j], acc, 0, 0, 0);
+  }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[8 * bb + pp] = fmaf(xf[e], wf[pp][e], acc[8 * bb + pp]);
+  for (int e = 0; e < 16; ++e) part[wave][e][lane] = acc[e];
+  __syncthreads();
+  // Accumulator e of lane l is q'[b0 + 8*(e/4) + 4*(l/32) + e%4][p0 + l%32].
+  {
+    const int e = tid / kWave, l = tid % kWave;  // 1024 threads, 16 x 64 outputs
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][l];
+    const long long b = b0 + 8 * (e / 4) + 4 * (l / 32) + (e % 4);
+    const int pp = p0 + (l & 31);
+    if (b < B && pp < P) q[(size_t)b * (size_t)P + pp] = v;
+    // For the fold: q' split exactly into three bf16 parts, row b of `parts`
+    // holding hi | mid | lo, each padded with zeros to a multiple of 16.
+    const int p16 = (P + 15) / 16 * 16;
+    if (parts != nullptr && b < B && pp < p16) {
+      float3 sp = make_float3(0.0f, 0.0f, 0.0f);
+      uint16_t* row = parts + (size_t)b * (size_t)(3 * p16);
+      if (pp < P) sp = split3(v);
+      row[pp] = bf16_bits(sp.x);
+      row[p16 + pp] = bf16_bits(sp.y);
+      row[2 * p16 + pp] = bf16_bits(sp.z);
     }
   }
-  const float total = wave_reduce_transposed<64>(acc, lane, OpSum());
-  const long long b = b0 + lane / 8;
-  const int p = p0 + lane % 8;
-  if (b < B && p < P) q[(size_t)b * (size_t)P + p] = total;
 }
 
 // u[b][h] = sum_p q'[b][p] * w[p][h]  (q' [B][P] fp32, w [P][H] bf16,
-// P <= 256, H % 8 == 0). A workgroup computes 4 questions x 512 consecutive
-// h; lane l owns h = 8l .. 8l+7. The feature sum is split over the 4 waves
-// (wave w takes features p = w, w+4, ...), each reading one 16-byte piece of
-// weight row p per step (1 KiB contiguous across the wave) and the 4
-// questions' q'[.][p] as one broadcast LDS read; the four partial sums are
-// then added in wave order through LDS.
-__global__ __launch_bounds__(256) void fold_query(const float* __restrict__ q,
-                                                  const uint16_t* __restrict__ w,
-                                                  float* __restrict__ u, int B, int H, int P) {
-  __shared__ float4 qs[256];              // q'[b0 .. b0+3][p] as one float4 per p
-  __shared__ float part[4][4][8][kWave];  // [wave][question][element][lane]
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int htiles = (H + 8 * kWave - 1) / (8 * kWave);
-  const long long b0 = ((long long)blockIdx.x / htiles) * 4;
-  const int h = (int)(blockIdx.x % htiles) * 8 * kWave + 8 * lane;
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    float v[4];
+// P <= 256, H % 8 == 0) on the bf16 matrix cores, from the three-part split
+// of q' that proj_query_mfma wrote (parts [B][3 * P16], P16 = P rounded up
+// to 16): the three products with a bf16 weight are exact and only the fp32
+// accumulation rounds, as in an fp32 dot product.
+//
+// Workgroup: 4 waves, 32 questions x 128 h; wave w takes columns
+// 32w .. +32. Both operands are staged in LDS first, with loads in which
+// consecutive lanes read consecutive bytes (a 16-byte-per-lane load that
+// touches 32 rows costs the L1 one tag lookup per row):
+//  * the questions' parts rows go in by DMA (global_load_lds_dwordx4), as
+//    blocks of 64 bf16 x 32 rows with the XOR swizzle of the ring kernel;
+//  * the contraction runs over p, the row index of w, so the 128 columns of
+//    w are staged transposed ([h][p], one 8 x 8 block of bf16 per thread,
+//    transposed in registers); weight fragments are then 16-byte reads.
+constexpr int kFoldRow = 256 + 8;              // bf16 per transposed row (p), padded
+constexpr int kFoldBlocks = 3 * 256 / 64;      // 64-wide blocks of a parts row, at most
+__shared__ __attribute__((aligned(1024))) uint8_t g_fold_a[kFoldBlocks][32 * 128];
+
+__global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restrict__ parts,
+                                                       const uint16_t* __restrict__ w,
+                                                       float* __restrict__ u, int B, int H,
+                                                       int P) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[128 * kFoldRow];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int htiles = (H + 127) / 128;
+  const long long b0 = (long long)(blockIdx.x / htiles) * 32;
+  const int h0 = (int)(blockIdx.x % htiles) * 128;
+  const int p16 = (P + 15) / 16 * 16;
+  const int kq = 3 * p16;                       // bf16 per parts row
+  const int nblk = (kq + 63) / 64;
+  // Weight loads first (their registers are waited on before the transposed
+  // stores; the DMAs issued after them stay in flight).
+  // Task (pg, hg) moves w[8pg .. +8][h0 + 8hg .. +8] to wt[8hg .. +8][8pg .. +8].
+  // In a wave, 8 lanes take consecutive hg (128 contiguous bytes of a row)
+  // and 8 take consecutive pg; rows of w past P and columns past H are zero.
+  const int npg = p16 / 8;
+  constexpr int kTasks = 2;  // per thread: 32 pg x 16 hg at P16 = 256
+  uint4 v[kTasks][8];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      v[bb] = (b0 + bb < B) ? q[(size_t)(b0 + bb) * (size_t)P + p] : 0.0f;
-    qs[p] = make_float4(v[0], v[1], v[2], v[3]);
+  for (int i = 0; i < kTasks; ++i) {
+    const int t = tid + 256 * i, blk = t / 64, tl = t % 64;
+    const int hg = 8 * (blk & 1) + (tl & 7), pg = 8 * (blk >> 1) + (tl >> 3);
+    const int hh = h0 + 8 * hg;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int pr = 8 * pg + r;
+      v[i][r] = (pg < npg && pr < P && hh < H)
+                    ? *reinterpret_cast<const uint4*>(w + (size_t)pr * (size_t)H + hh)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
-  __syncthreads();
-  float acc[4][8];
+  // Parts DMA: block kb, rows 8j .. +8 of the 32; wave w issues blocks
+  // w, w+4, ... (each 4 instructions). Lane l fills position l % 8 of row
+  // 8j + l / 8 with logical piece swizzled_piece(row, l % 8).
+  for (int kb = wave; kb < nblk; kb += 4) {
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0f;
-  if (h < H) {
-#pragma unroll 4
-    for (int p = wave; p < P; p += 4) {
-      const uint4 v = load_piece<false>(w + (size_t)p * (size_t)H + h);
-      const float wf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-      const float4 qv = qs[p];
-      const float qb[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(qb[bb], wf[e], acc[bb][e]);
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * j + lane / 8;
+      const int k = 64 * kb + 8 * swizzled_piece(row, lane % 8);
+      const uint16_t* src = parts + (size_t)min(b0 + row, (long long)B - 1) * (size_t)kq +
+                            (k < kq ? k : 0);
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(g_fold_a[kb] + 1024 * j), 16,
+                                       0, 0);
     }
   }
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
+  for (int i = 0; i < kTasks; ++i) {
+    const int t = tid + 256 * i, blk = t / 64, tl = t % 64;
+    const int hg = 8 * (blk & 1) + (tl & 7), pg = 8 * (blk >> 1) + (tl >> 3);
+    if (pg >= npg) continue;
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(v[i]);  // vw[4r + c/2] = w[r][c]
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[wave][bb][e][lane] = acc[bb][e];
+    for (int c = 0; c < 8; ++c) {
+      uint32_t o[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t e0 = vw[4 * (2 * jj) + c / 2], e1 = vw[4 * (2 * jj + 1) + c / 2];
+        o[jj] = (c & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
+      }
+      *reinterpret_cast<uint4*>(&wt[(8 * hg + c) * kFoldRow + 8 * pg]) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  wait_vmcnt<0>();
   __syncthreads();
-  // wave w now finishes question b0 + w
-  const long long b = b0 + wave;
-  if (b >= B || h >= H) return;
-  float r[8];
+  const int r = lane & 31, half = lane >> 5;
+  const uint32_t abase = lds_address(g_fold_a[0]);
+  const uint16_t* wrow = &wt[(32 * wave + r) * kFoldRow + 8 * half];
+  // One accumulator per part, so the three products of a step are
+  // independent and share the weight fragment. Every lane runs the same steps
+  // (the matrix instructions need the whole wave); in step s, lane half h
+  // feeds features 16s + 8h .. +8, which sit at k = c * P16 + 16s + 8h of
+  // the parts row for part c. Four steps' reads are issued before one wait.
+  f32x16_t acc[3];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    r[e] = ((part[0][wave][e][lane] + part[1][wave][e][lane]) + part[2][wave][e][lane]) +
-           part[3][wave][e][lane];
-  float4* dst = reinterpret_cast<float4*>(u + (size_t)b * (size_t)H + h);
-  dst[0] = make_float4(r[0], r[1], r[2], r[3]);
-  dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+  for (int c = 0; c < 3; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+  for (int kb0 = 0; kb0 < p16; kb0 += 64) {
+    bf16x8_t af[4][3], wf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = kb0 + 16 * j;
+      if (k0 < p16) {  // uniform
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const int k = c * p16 + k0 + 8 * half;
+          lds_fragment<0>(af[j][c], abase + (uint32_t)((k / 64) * (32 * 128) + r * 128 +
+                                                       16 * swizzled_piece(r, (k % 64) / 8)));
+        }
+        lds_fragment<0>(wf[j], lds_address(reinterpret_cast<const uint8_t*>(wrow + k0)));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kb0 + 16 * j < p16) {
+        asm volatile("" : "+v"(af[j][0]), "+v"(af[j][1]), "+v"(af[j][2]), "+v"(wf[j]));
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j][c], wf[j], acc[c], 0, 0, 0);
+      }
+    }
+  }
+  // Accumulator e of lane l: question b0 + 8*(e/4) + 4*(l/32) + e%4, column
+  // h0 + 32*wave + l%32.
+  const int hcol = h0 + 32 * wave + (lane & 31);
+  if (hcol >= H) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const long long b = b0 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+    if (b < B) u[(size_t)b * (size_t)H + hcol] = acc[0][e] + (acc[1][e] + acc[2][e]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -427,25 +592,6 @@ __device__ __forceinline__ uint8_t* stage_tile() {
   return W ? g_ws[S] : g_xs[S];
 }
 
-typedef __attribute__((address_space(1))) const void* global_ptr_t;
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Physical 16-byte position of logical piece `piece` of row `row`. The
-// mapping depends on row % 16 only (so the 32-row blocks a lane reads share
-// it), and any 16 consecutive rows reading the same logical piece hit
-// distinct banks.
-__device__ __forceinline__ int swizzled_piece(int row, int piece) {
-  return piece ^ ((row & 7) ^ ((row >> 3) & 1));
-}
-
-// s_waitcnt with only the vector-memory count limited to n (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Workgroup barrier for the stage ring: this wave's LDS reads are complete
 // (lgkmcnt 0) before it arrives, and no memory access is moved across it by
 // the compiler. Unlike __syncthreads it does not wait for the DMA loads still
@@ -480,20 +626,6 @@ __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* w
                                      (lds_ptr_t)(stage_tile<S, true>() + r0 * kARowBytes), 16, 0,
                                      0);
   }
-}
-
-__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-// One 16-byte fragment read from LDS at byte address addr + OFF. Written as
-// inline assembly so that the compiler, which cannot always tell which DMA
-// stage a read depends on, does not add a wait for every DMA in flight; the
-// ring's own vmcnt waits and barriers order the reads instead. The result is
-// not ready until lds_fragments_ready().
-template <int OFF>
-__device__ __forceinline__ void lds_fragment(bf16x8_t& f, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
 
 // Waits for every fragment read issued so far and makes each fragment a
@@ -776,11 +908,11 @@ int bf16_nv_for(int Hc) {
 }
 
 hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
-  // q' = Wq x_q for every question: one wave per 8 x 8 tile.
+  // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
   {
-    const long long waves = (long long)((p.B + 7) / 8) * ((p.P + 7) / 8);
-    hipLaunchKernelGGL(proj_query, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, p.xq,
-                       p.wq, p.qp, p.B, p.Hq, p.P);
+    const long long groups = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
+    hipLaunchKernelGGL(proj_query_mfma, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream,
+                       p.xq, p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -794,12 +926,12 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.zscale = p.zscale;
   a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
-  // u = Wc^T q' (one workgroup per 4 questions x 512 h), then one
+  // u = Wc^T q' (one workgroup per 32 questions x 128 h), then one
   // bandwidth-bound pass over the candidates.
   {
-    const long long groups = (long long)((p.B + 3) / 4) * ((p.Hc + 511) / 512);
-    hipLaunchKernelGGL(fold_query, dim3((unsigned)groups), dim3(256), 0, stream, p.qp, p.wc, p.u,
-                       p.B, p.Hc, p.P);
+    const long long groups = (long long)((p.B + 31) / 32) * ((p.Hc + 127) / 128);
+    hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)groups), dim3(256), 0, stream, p.parts,
+                       p.wc, p.u, p.B, p.Hc, p.P);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;

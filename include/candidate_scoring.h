@@ -171,8 +171,9 @@ int cs_score_candidates_ragged(const float *queries, const float *candidates,
  * (c' . q' = x . (Wc^T q')), so candidates are read once and never projected;
  * for cosine, each question's projected candidates are computed on the
  * matrix cores and reduced to their similarity in registers. The workspace
- * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected (and
- * folded) queries. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
+ * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected
+ * queries and, for dot, the folded queries and an exact three-part bf16
+ * split of the projected ones. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
  * 16-byte aligned inputs, P a multiple of 64 for cosine, Hc <= 4096 for dot;
  * other valid sizes return CS_ERR_UNSUPPORTED. Enqueues two (cosine) or
  * three (dot) kernels on `stream`. */
