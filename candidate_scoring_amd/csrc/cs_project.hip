@@ -860,8 +860,8 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
     case 1: return launch_bf16_dot_nv<1, 8, NT>(a, p, grid, block, stream);
     case 2: return launch_bf16_dot_nv<2, 4, NT>(a, p, grid, block, stream);
     case 3: return launch_bf16_dot_nv<3, 4, NT>(a, p, grid, block, stream);
-    case 4: return launch_bf16_dot_nv<4, 2, NT>(a, p, grid, block, stream);
-    case 5: return launch_bf16_dot_nv<5, 2, NT>(a, p, grid, block, stream);
+    case 4: return launch_bf16_dot_nv<4, 4, NT>(a, p, grid, block, stream);
+    case 5: return launch_bf16_dot_nv<5, 4, NT>(a, p, grid, block, stream);
     case 6: return launch_bf16_dot_nv<6, 2, NT>(a, p, grid, block, stream);
     case 8: return launch_bf16_dot_nv<8, 2, NT>(a, p, grid, block, stream);
     default: return hipErrorInvalidValue;
@@ -896,7 +896,7 @@ hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t s
 
 }  // namespace
 
-int bf16_rows_per_wave(int nv) { return nv <= 1 ? 8 : nv <= 3 ? 4 : 2; }
+int bf16_rows_per_wave(int nv) { return nv <= 1 ? 8 : nv <= 5 ? 4 : 2; }
 
 int bf16_nv_for(int Hc) {
   const int pieces = Hc / 8;
