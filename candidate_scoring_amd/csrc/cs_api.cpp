@@ -262,9 +262,6 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   const int mean_k = (int)std::max<long long>(1, total_rows / B);
   cs::LaunchShape ls = make_shape(B, mean_k, D, 1, CS_MAX_K, Q, C);
   ls.nt = 4.0 * (double)total_rows * (double)D >= kStreamBytes ? 1 : 0;
-  // The scheduled kernels run at three waves per SIMD; four-wave workgroups
-  // keep three of them resident per CU.
-  if (a.longest_first) ls.block = std::min<unsigned>(ls.block, 4 * kWave);
   const hipError_t err = cs::launch_fused(a, ls, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;

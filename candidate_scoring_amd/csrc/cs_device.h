@@ -218,8 +218,13 @@ __device__ __forceinline__ bool resolve_question(const KernelArgs& a, int b, int
     if (tid == 0 && a.status != nullptr) *a.status = kStatusBadOffsets;
     return false;
   }
-  qn.row = (size_t)lo;
-  qn.K = (int)(hi - lo);
+  // Uniform across the workgroup; saying so keeps the row addresses in
+  // scalar registers.
+  const unsigned long long row = (unsigned long long)lo;
+  qn.row = (size_t)(((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(
+                         (int)(row >> 32)) << 32) |
+                    (unsigned)__builtin_amdgcn_readfirstlane((int)(row & 0xffffffffu)));
+  qn.K = __builtin_amdgcn_readfirstlane((int)(hi - lo));
   return true;
 }
 
@@ -246,12 +251,33 @@ __device__ __forceinline__ int question_of_rank(const KernelArgs& a, int rank, L
 #pragma unroll 1
   for (int b = tid; b < a.B; b += nt) atomicAdd(&s.hist[count_key(a, b)], 1);
   __syncthreads();
-  if (tid == 0) {
-    int before = 0, key = 0;
-#pragma unroll 1
-    for (; key < kMaxSlots - 1 && rank >= before + s.hist[key]; ++key) before += s.hist[key];
-    s.pick[0] = key;
-    s.pick[1] = rank - before;  // position among the questions with this key
+  // Wave 0 finds the key class holding `rank`: lane l owns keys 4l .. 4l+3,
+  // an inclusive scan of the per-lane counts brackets the rank, and the one
+  // lane whose bracket holds it walks its four keys.
+  if (wave == 0) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = s.hist[4 * lane + i];
+      sum += c[i];
+    }
+    int incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
+    int before = incl - sum;
+    if (rank >= before && rank < incl) {
+      int key = 4 * lane;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (rank < before + c[i]) break;
+        before += c[i];
+        ++key;
+      }
+      s.pick[0] = key;
+      s.pick[1] = rank - before;  // position among the questions with this key
+    }
   }
   __syncthreads();
   const int key = s.pick[0], j = s.pick[1];
@@ -314,7 +340,8 @@ __device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k
 // Softmax of this slice's n logits (wave 0 only) and the store of either the
 // final probabilities (one slice per question) or the unnormalised e_k plus
 // the slice's (max, sum) partial.
-template <bool COS>
+// MAYSPLIT = false: the caller never splits a question (a.G is 1).
+template <bool COS, bool MAYSPLIT = true>
 __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
                                               int b, int g, int r0, int n, float zfac,
                                               int lane) {
@@ -351,7 +378,7 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
   }
   l = wave_allreduce(l, lane, OpSum());
   float* out = a.out + qn.row + r0;
-  if (a.G == 1) {
+  if (!MAYSPLIT || a.G == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = lane + kWave * i;

@@ -69,17 +69,19 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int D4 = a.D >> 2;
-  const long long items = (long long)a.B * a.G;
+  // A ragged batch is never split: one item per question.
+  const int G = RAGGED ? 1 : a.G;
+  const long long items = (long long)a.B * G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
-    int b = (int)(item / a.G);
+    int b = (int)(item / G);
     if constexpr (RAGGED) {
       if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
     }
-    const int g = (int)(item % a.G);
+    const int g = (int)(item % G);
     Question qn;
     if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
-    const int r0 = g * a.rpg;
-    const int r1 = min(qn.K, r0 + a.rpg);
+    const int r0 = RAGGED ? 0 : g * a.rpg;
+    const int r1 = RAGGED ? qn.K : min(qn.K, r0 + a.rpg);
     const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
     float4 qr[NV];
 #pragma unroll
@@ -127,9 +129,9 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         qq = wave_allreduce(qq, lane, OpSum());
         zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
       }
-      slice_softmax<COS>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
+      slice_softmax<COS, !RAGGED>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
     }
-    if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+    if (!RAGGED && a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
 }
@@ -151,17 +153,19 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   constexpr int V = COS ? 2 * R : R;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
-  const long long items = (long long)a.B * a.G;
+  // A ragged batch is never split: one item per question.
+  const int G = RAGGED ? 1 : a.G;
+  const long long items = (long long)a.B * G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
-    int b = (int)(item / a.G);
+    int b = (int)(item / G);
     if constexpr (RAGGED) {
       if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
     }
-    const int g = (int)(item % a.G);
+    const int g = (int)(item % G);
     Question qn;
     if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
-    const int r0 = g * a.rpg;
-    const int r1 = min(qn.K, r0 + a.rpg);
+    const int r0 = RAGGED ? 0 : g * a.rpg;
+    const int r1 = RAGGED ? qn.K : min(qn.K, r0 + a.rpg);
     const float* qb = a.Q + (size_t)b * (size_t)a.D;
     const float* Cb = a.C + qn.row * (size_t)a.D;
     const bool need_qq = COS || (a.cosine && a.staged_norms != nullptr);
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
     } else {
       __syncthreads();
     }
-    if (wave == 0) slice_softmax<COS>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
-    if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+    if (wave == 0) slice_softmax<COS, !RAGGED>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
+    if (!RAGGED && a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
 }
