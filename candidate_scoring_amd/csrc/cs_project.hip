@@ -603,18 +603,18 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// DMA of hidden chunk c into stage S: this wave fills rows 32*wave .. +32 of
-// the X tile and of the W tile. X rows past K repeat row K-1 and W rows past
-// P repeat row P-1; those rows are never read. (The helpers take plain
-// pointers: restrict-qualified parameters of an inlined function would give
-// every call site alias scopes of its own.)
-template <int S, bool NT>
+// DMA of hidden chunk c into stage S: this wave fills rows RPW*wave .. +RPW
+// of the X tile and of the W tile (RPW = 256 / waves). X rows past K repeat
+// row K-1 and W rows past P repeat row P-1; those rows are never read. (The
+// helpers take plain pointers: restrict-qualified parameters of an inlined
+// function would give every call site alias scopes of its own.)
+template <int S, int RPW, bool NT>
 __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* wc, int c, int K,
                                            int P, int H, int wave, int lane) {
   const int h0 = c * kAChunk;
 #pragma unroll
-  for (int j = 0; j < 32 / kARowsPerLoad; ++j) {
-    const int r0 = 32 * wave + kARowsPerLoad * j;
+  for (int j = 0; j < RPW / kARowsPerLoad; ++j) {
+    const int r0 = RPW * wave + kARowsPerLoad * j;
     const int row = r0 + lane / kAPieces;
     const int piece = swizzled_piece(row, lane % kAPieces);
     const uint16_t* src = Xb + (size_t)min(row, K - 1) * (size_t)H + h0 + 8 * piece;
@@ -628,29 +628,40 @@ __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* w
   }
 }
 
+// Fragment reads of one 16-wide step: N 32-row blocks, 4 KiB apart, starting
+// at byte address addr (the offsets are immediates of the instruction).
+template <int N>
+__device__ __forceinline__ void lds_blocks(bf16x8_t (&f)[N], uint32_t addr) {
+  static_assert(N >= 1 && N <= 4, "blocks per step");
+  lds_fragment<0>(f[0], addr);
+  if constexpr (N > 1) lds_fragment<32 * kARowBytes>(f[N > 1 ? 1 : 0], addr);
+  if constexpr (N > 2) lds_fragment<64 * kARowBytes>(f[N > 2 ? 2 : 0], addr);
+  if constexpr (N > 3) lds_fragment<96 * kARowBytes>(f[N > 3 ? 3 : 0], addr);
+}
+
 // Waits for every fragment read issued so far and makes each fragment a
 // result of the wait, so nothing that uses one can be scheduled before it.
-template <int TN>
-__device__ __forceinline__ void lds_fragments_ready(bf16x8_t (&af)[2], bf16x8_t (&bfr)[TN]) {
+template <int RB, int TN>
+__device__ __forceinline__ void lds_fragments_ready(bf16x8_t (&af)[RB], bf16x8_t (&bfr)[TN]) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) asm volatile("" : "+v"(af[rb]));
+  for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(af[rb]));
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(bfr[tn]));
 }
 
-// Per-lane byte offsets of the two 16-wide steps of a chunk inside an X tile
-// (rows 64*wr + lane%32, +32) and a W tile (rows 32*TN*wcb + lane%32, +32,
-// ...). The swizzle depends on row % 16 only, so the 32-row blocks of one
-// lane share it and sit 2 KiB apart.
+// Per-lane byte offsets of the 16-wide steps of a chunk inside an X tile
+// (rows 32*RB*wr + lane%32, +32, ...) and a W tile (rows 32*TN*wcb + lane%32,
+// +32, ...). The swizzle depends on row % 16 only, so the 32-row blocks of
+// one lane share it and sit 4 KiB apart.
 struct StageOffsets {
   uint32_t x[kAKSteps], w[kAKSteps];
 };
 
-template <int TN>
+template <int TN, int RB>
 __device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int wcb) {
   StageOffsets o;
-  const int rx = 64 * wr + (lane & 31), rw = 32 * TN * wcb + (lane & 31);
+  const int rx = 32 * RB * wr + (lane & 31), rw = 32 * TN * wcb + (lane & 31);
 #pragma unroll
   for (int ks = 0; ks < kAKSteps; ++ks) {
     const int piece = 2 * ks + (lane >> 5);
@@ -660,27 +671,33 @@ __device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int wcb)
   return o;
 }
 
-template <int S, int TN>
-__device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[2][TN], const StageOffsets& o) {
+// The matrix-core work of one chunk: RB x TN accumulators, four 16-wide
+// steps. The fragments of step ks+1 are read while the matrix cores work on
+// step ks (scheduling barriers keep the compiler from merging the phases).
+template <int S, int TN, int RB>
+__device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[RB][TN], const StageOffsets& o) {
   const uint32_t xs = lds_address(stage_tile<S, false>());
   const uint32_t ws = lds_address(stage_tile<S, true>());
+  bf16x8_t af[2][RB], bfr[2][TN];
+  lds_blocks<RB>(af[0], xs + o.x[0]);
+  lds_blocks<TN>(bfr[0], ws + o.w[0]);
+  lds_fragments_ready<RB, TN>(af[0], bfr[0]);
 #pragma unroll
   for (int ks = 0; ks < kAKSteps; ++ks) {
-    bf16x8_t af[2], bfr[TN];
-    const uint32_t xa = xs + o.x[ks], wa = ws + o.w[ks];
-    lds_fragment<0>(af[0], xa);
-    lds_fragment<32 * kARowBytes>(af[1], xa);
-    lds_fragment<0>(bfr[0], wa);
-    if constexpr (TN > 1) lds_fragment<32 * kARowBytes>(bfr[TN > 1 ? 1 : 0], wa);
-    if constexpr (TN > 2) lds_fragment<64 * kARowBytes>(bfr[TN > 2 ? 2 : 0], wa);
-    if constexpr (TN > 3) lds_fragment<96 * kARowBytes>(bfr[TN > 3 ? 3 : 0], wa);
-    lds_fragments_ready<TN>(af, bfr);
+    const int cur = ks & 1;
+    if (ks + 1 < kAKSteps) {
+      lds_blocks<RB>(af[cur ^ 1], xs + o.x[ks + 1]);
+      lds_blocks<TN>(bfr[cur ^ 1], ws + o.w[ks + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        acc[rb][tn] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[tn], acc[rb][tn], 0, 0, 0);
+        acc[rb][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][rb], bfr[cur][tn],
+                                                              acc[rb][tn], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + 1 < kAKSteps) lds_fragments_ready<RB, TN>(af[cur ^ 1], bfr[cur ^ 1]);
   }
 }
 
@@ -689,11 +706,12 @@ __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[2][TN], const StageOf
 // c+1, multiply chunk c. Chunk c+1 may be the first of the next question of
 // this workgroup (Xn; null when there is none or when questions do not carry
 // the ring). The step with c < 0 only fills (the start of the ring).
-template <int S, int TN, bool NT>
-__device__ __forceinline__ void stage_step(f32x16_t (&acc)[2][TN], const StageOffsets& o,
+template <int S, int TN, int RB, bool NT>
+__device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageOffsets& o,
                                            const uint16_t* Xb, const uint16_t* Xn,
                                            const uint16_t* wc, int c, int nchunks, int K, int H,
                                            int wave, int lane) {
+  constexpr int kWaves = 16 / RB;  // 4 x 2 (RB = 2) or 2 x 2 (RB = 4) tiles of the output
   if (c >= nchunks) return;
   if (c >= 0) {
     // With two stages the only chunk in flight is c itself (issued at the
@@ -708,8 +726,9 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[2][TN], const StageOf
     src = Xn;
   }
   if (next >= 0 && src != nullptr)
-    stage_fill<(S + kAStages - 1) % kAStages, NT>(src, wc, next, K, 64 * TN, H, wave, lane);
-  if (c >= 0) stage_mfma<S, TN>(acc, o);
+    stage_fill<(S + kAStages - 1) % kAStages, 256 / kWaves, NT>(src, wc, next, K, 64 * TN, H,
+                                                                wave, lane);
+  if (c >= 0) stage_mfma<S, TN, RB>(acc, o);
 }
 
 // DMA of the current question's q' (P floats) into g_qp by one wave: lane l
@@ -737,9 +756,9 @@ __device__ __forceinline__ void lds_values_ready(float (&v)[N]) {
 // vector-memory counter) and barriers that do not wait for the next
 // question's DMAs already in flight. The ring's last wait covered the q' DMA,
 // which wave 0 issued before the question's later chunks.
-template <int TN>
+template <int TN, int RB>
 __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
-                                                  const f32x16_t (&acc)[2][TN], int b, int K,
+                                                  const f32x16_t (&acc)[RB][TN], int b, int K,
                                                   int lane, int wave, int wr, int wcb) {
   const uint32_t qbase = lds_address(reinterpret_cast<const uint8_t*>(g_qp));
   float qv[TN];
@@ -747,34 +766,47 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
   for (int tn = 0; tn < TN; ++tn)
     lds_value(qv[tn], qbase + 4u * (uint32_t)(32 * TN * wcb + 32 * tn + (lane & 31)));
   lds_values_ready<TN>(qv);
-  float dv[32], ev[32];
+  // Accumulator e of tile (rb, tn) in lane l holds C'[row][col] with
+  // row = 32*RB*wr + 32*rb + 8*(e/4) + 4*(l/32) + e%4 and
+  // col = 32*TN*wcb + 32*tn + l%32; pairs of row blocks are reduced at once.
+  float dsum[RB / 2], esum[RB / 2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int pr = 0; pr < RB / 2; ++pr) {
+    float dv[32], ev[32];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float d = 0.0f, q2 = 0.0f;
+    for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const float c = acc[rb][tn][e];
-        d = fmaf(c, qv[tn], d);
-        q2 = fmaf(c, c, q2);
+      for (int e = 0; e < 16; ++e) {
+        float d = 0.0f, q2 = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const float c = acc[2 * pr + r2][tn][e];
+          d = fmaf(c, qv[tn], d);
+          q2 = fmaf(c, c, q2);
+        }
+        dv[16 * r2 + e] = d;
+        ev[16 * r2 + e] = q2;
       }
-      dv[16 * rb + e] = d;
-      ev[16 * rb + e] = q2;
-    }
-  const float dsum = halfwave_reduce_transposed<32>(dv, lane, OpSum());
-  const float esum = halfwave_reduce_transposed<32>(ev, lane, OpSum());
-  const int v = lane & 31, rb = v >> 4, e = v & 15;
-  const int row = 64 * wr + 32 * rb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    dsum[pr] = halfwave_reduce_transposed<32>(dv, lane, OpSum());
+    esum[pr] = halfwave_reduce_transposed<32>(ev, lane, OpSum());
+  }
+  const int v = lane & 31, e = v & 15;
+  const int row0 = 32 * RB * wr + 32 * (v >> 4) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
   // The two column halves of a row are added in a fixed order.
   if (wcb == 0) {
-    s.dot[row] = dsum;
-    s.ss[row] = esum;
+#pragma unroll
+    for (int pr = 0; pr < RB / 2; ++pr) {
+      s.dot[row0 + 64 * pr] = dsum[pr];
+      s.ss[row0 + 64 * pr] = esum[pr];
+    }
   }
   stage_barrier();
   if (wcb == 1) {
-    s.dot[row] += dsum;
-    s.ss[row] += esum;
+#pragma unroll
+    for (int pr = 0; pr < RB / 2; ++pr) {
+      s.dot[row0 + 64 * pr] += dsum[pr];
+      s.ss[row0 + 64 * pr] += esum[pr];
+    }
   }
   stage_barrier();
   if (wave == 0) {
@@ -795,43 +827,46 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
 }
 
 // A workgroup takes questions blockIdx.x, blockIdx.x + gridDim.x, ... and,
-// when the chunk count is a multiple of the stage count, keeps the ring
-// running across them: the first three chunks of the next question are in
-// flight during the last steps and the epilogue of the current one.
-template <int TN, bool NT>
-__global__ __launch_bounds__(512) void proj_cos_mfma_async(KernelArgs a,
-                                                           const uint16_t* __restrict__ xc,
-                                                           const uint16_t* __restrict__ wc,
-                                                           const float* __restrict__ qp) {
+// when the chunk count is even, keeps the ring running across them: the first
+// chunk of the next question is in flight during the last step and the
+// epilogue of the current one. RB = 2: 8 waves, each 64 rows x 32*TN
+// features; RB = 4: 4 waves, each 128 rows x 32*TN features (fewer fragment
+// reads per matrix instruction, one wave per SIMD).
+template <int TN, bool NT, int RB>
+__global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
+    KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
+    const float* __restrict__ qp) {
   static_assert(kAStages == 2, "the chunk loop is unrolled by the stage count");
+  static_assert(RB == 2 || RB == 4, "row blocks per wave");
+  constexpr int kRowGroups = 8 / RB;
   __shared__ Lds s;
   constexpr int P = 64 * TN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wr = wave & 3, wcb = wave >> 2;
+  const int wr = wave % kRowGroups, wcb = wave / kRowGroups;
   const int H = a.D, K = a.K;
   const int nchunks = H / kAChunk;
   const bool carry = nchunks % kAStages == 0;
   const int stride = (int)gridDim.x;
-  const StageOffsets o = stage_offsets<TN>(lane, wr, wcb);
+  const StageOffsets o = stage_offsets<TN, RB>(lane, wr, wcb);
   for (int b = blockIdx.x; b < a.B; b += stride) {
     const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
     const uint16_t* Xn =
         (carry && b + stride < a.B) ? xc + (size_t)(b + stride) * (size_t)K * (size_t)H : nullptr;
     if (wave == 0) qp_fill(qp + (size_t)b * P, P, lane);
-    f32x16_t acc[2][TN];
+    f32x16_t acc[RB][TN];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
     if (!carry || b == (int)blockIdx.x)
-      stage_step<1, TN, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane);
+      stage_step<1, TN, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane);
     for (int c = 0; c < nchunks; c += kAStages) {
-      stage_step<0, TN, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane);
-      stage_step<1, TN, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane);
+      stage_step<0, TN, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane);
+      stage_step<1, TN, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane);
     }
-    cos_epilogue_ring<TN>(s, a, acc, b, K, lane, wave, wr, wcb);
+    cos_epilogue_ring<TN, RB>(s, a, acc, b, K, lane, wave, wr, wcb);
   }
 }
 
@@ -868,14 +903,19 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
   }
 }
 
+// Eight waves of 64-row tiles. (Four waves of 128-row tiles would need fewer
+// fragment reads per matrix instruction, but their 256 accumulators leave
+// too few vector registers and the compiler spills.)
+constexpr int kCosRowBlocks = 2;
+
 template <int TN, bool NT>
 void launch_cos_tile(const KernelArgs& a, const ProjArgs& p, unsigned grid, hipStream_t stream) {
   if (p.Hc % kAChunk == 0)
     // One resident workgroup per compute unit (its LDS allows no more), each
     // working through its share of the questions.
-    hipLaunchKernelGGL((proj_cos_mfma_async<TN, NT>),
+    hipLaunchKernelGGL((proj_cos_mfma_async<TN, NT, kCosRowBlocks>),
                        dim3(p.compute_units > 0 ? std::min(grid, (unsigned)p.compute_units) : grid),
-                       dim3(512), 0, stream, a, p.xc, p.wc, p.qp);
+                       dim3(64 * (16 / kCosRowBlocks)), 0, stream, a, p.xc, p.wc, p.qp);
   else
     hipLaunchKernelGGL((proj_cos_mfma<TN, NT>), dim3(grid), dim3(512), 0, stream, a, p.xc, p.wc,
                        p.qp);
