@@ -348,32 +348,32 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
 // ---------------------------------------------------------------------------
 // Dot scoring of bf16 candidate rows against the folded fp32 query u: the
 // register-query kernel's structure with 16-byte pieces of 8 bf16. Lane l
-// owns pieces l + 64 j (j < NV) of u and of every row; a wave takes R rows at
-// a time; one workgroup per question.
+// owns pieces l + 64 j (j < NV) of every row; a wave takes R rows at a time;
+// one workgroup per question. u sits in LDS (its low and high halves of each
+// piece in two arrays, so a wave's reads are contiguous) rather than in 8*NV
+// registers per lane, which leaves room for more loads in flight.
 template <int NV, int R, bool FULL, bool NT>
 __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
                                                          const uint16_t* __restrict__ xc,
                                                          const float* __restrict__ u) {
   __shared__ Lds s;
+  __shared__ float4 us_lo[8 * kWave], us_hi[8 * kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int pieces = a.D >> 3;
   for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
     const Question qn{(size_t)b * (size_t)a.K, a.K};
-    float ur[NV][8];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int idx = lane + kWave * j;
+    for (int idx = tid; idx < NV * kWave; idx += blockDim.x) {
+      float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
       if (FULL || idx < pieces) {
         const float4* up = reinterpret_cast<const float4*>(u + (size_t)b * (size_t)a.D) + 2 * idx;
-        const float4 u0 = up[0], u1 = up[1];
-        ur[j][0] = u0.x; ur[j][1] = u0.y; ur[j][2] = u0.z; ur[j][3] = u0.w;
-        ur[j][4] = u1.x; ur[j][5] = u1.y; ur[j][6] = u1.z; ur[j][7] = u1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ur[j][e] = 0.0f;
+        u0 = up[0];
+        u1 = up[1];
       }
+      us_lo[idx] = u0;
+      us_hi[idx] = u1;
     }
+    __syncthreads();
     const uint16_t* Xb = xc + qn.row * (size_t)a.D;
     for (int k0 = wave * R; k0 < a.K; k0 += nwaves * R) {
       float acc[R];
@@ -393,9 +393,12 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
                                            : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
+      for (int j = 0; j < NV; ++j) {
+        const float4 u0 = us_lo[lane + kWave * j], u1 = us_hi[lane + kWave * j];
+        const float ur[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = dot8_bf(c[r][j], ur[j], acc[r]);
+        for (int r = 0; r < R; ++r) acc[r] = dot8_bf(c[r][j], ur, acc[r]);
+      }
       const float total = wave_reduce_transposed<R>(acc, lane, OpSum());
       store_group<false, R>(s, total, lane, k0, 0, a.K);
     }
@@ -895,8 +898,8 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
     case 1: return launch_bf16_dot_nv<1, 8, NT>(a, p, grid, block, stream);
     case 2: return launch_bf16_dot_nv<2, 4, NT>(a, p, grid, block, stream);
     case 3: return launch_bf16_dot_nv<3, 4, NT>(a, p, grid, block, stream);
-    case 4: return launch_bf16_dot_nv<4, 4, NT>(a, p, grid, block, stream);
-    case 5: return launch_bf16_dot_nv<5, 4, NT>(a, p, grid, block, stream);
+    case 4: return launch_bf16_dot_nv<4, 2, NT>(a, p, grid, block, stream);
+    case 5: return launch_bf16_dot_nv<5, 2, NT>(a, p, grid, block, stream);
     case 6: return launch_bf16_dot_nv<6, 2, NT>(a, p, grid, block, stream);
     case 8: return launch_bf16_dot_nv<8, 2, NT>(a, p, grid, block, stream);
     default: return hipErrorInvalidValue;
@@ -936,7 +939,7 @@ hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t s
 
 }  // namespace
 
-int bf16_rows_per_wave(int nv) { return nv <= 1 ? 8 : nv <= 5 ? 4 : 2; }
+int bf16_rows_per_wave(int nv) { return nv <= 1 ? 8 : nv <= 3 ? 4 : 2; }
 
 int bf16_nv_for(int Hc) {
   const int pieces = Hc / 8;

@@ -80,7 +80,7 @@ def dev(cs):
     (3, 77, 520, 1000, 96, "dot"),
     (2, 255, 8, 8, 8, "dot"),
     (2, 100, 136, 4096, 256, "dot"),
-    (3, 255, 64, 2048, 64, "dot"),         # four 16-byte pieces per lane, four rows per wave
+    (3, 255, 64, 2048, 64, "dot"),         # four 16-byte pieces per lane
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
