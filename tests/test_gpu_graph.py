@@ -73,3 +73,64 @@ def test_workspace_init_kernel_zeroes(cs):
         assert cs.cs_workspace_init(buf, n) == 0
         torch.cuda.synchronize()
         assert torch.all(buf[:n] == 0) and torch.all(buf[n:] == 0xAB), n
+
+
+def _bits(b, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev)
+
+
+@pytest.mark.parametrize("kind", ["ragged", "projected_dot", "projected_cosine"])
+def test_capture_multi_kernel_paths_replay_exact(cs, kind):
+    """The ragged and projection entry points captured into a graph (through
+    torch's capture of the current stream) replay to exactly the direct
+    call's result, with eager work between replays."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    note(f"case graph {kind}")
+    if kind == "ragged":
+        offsets = workloads.ragged_offsets(71, 300)
+        Q, C = workloads.ragged_inputs(72, offsets, 520)
+        rows = int(offsets[-1])
+        q, c = torch.from_numpy(Q).to(dev), torch.from_numpy(C).to(dev)
+        o = torch.from_numpy(offsets).to(dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def run(out):
+            assert cs.cs_score_candidates_ragged(q, c, o, 300, rows, 520, "cosine",
+                                                 float(workloads.SCALE_COSINE), 1.0, out,
+                                                 status) == 0
+
+        shape = (rows,)
+    else:
+        sim = "dot" if kind == "projected_dot" else "cosine"
+        w = workloads.projected_inputs(73, 300, 40, 136, 256, 128, sim)
+        xq, xc = _bits(w.xq_bits, dev), _bits(w.xc_bits, dev)
+        wq, wc = _bits(w.wq_bits, dev), _bits(w.wc_bits, dev)
+        nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, sim)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+        def run(out):
+            assert cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, sim,
+                                         float(w.scale), 1.0, out, ws, nbytes) == 0
+
+        shape = (w.B, w.K)
+    direct = torch.empty(shape, device=dev)
+    run(direct)
+    torch.cuda.synchronize()
+    replayed = torch.full(shape, -1.0, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run(replayed)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        replayed.fill_(-1.0)
+        _ = (direct * 2).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, direct)
