@@ -81,6 +81,8 @@ def dev(cs):
     (2, 255, 8, 8, 8, "dot"),
     (2, 100, 136, 4096, 256, "dot"),
     (3, 255, 64, 2048, 64, "dot"),         # four 16-byte pieces per lane
+    (2, 50, 520, 1000, 200, "dot"),        # P not a multiple of 16 or 32
+    (1, 255, 4096, 4096, 256, "cosine"),   # one question, 64 chunks of the DMA ring
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
