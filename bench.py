@@ -13,7 +13,8 @@ Beside the headline it reports (same line):
     against the 8 TB/s HBM peak, and the HBM traffic measured by rocprofv3
     counters when the committed profile matches the current kernel source;
   * latency: single-question and small-batch calls timed through hipGraph
-    replay (2000 replays of a one-node graph, the page's protocol) next to an
+    replay (2000 replays of a one-node graph in five repetitions, the page's
+    protocol; median and min per call) next to an
     empty kernel of the same grid and block replayed the same way: the launch
     floor;
   * cpu_baseline: the double-precision oracle on the host, single-threaded
@@ -158,6 +159,9 @@ class Device:
         return ms.value
 
 
+LATENCY_REPS = 5
+
+
 def latency_section(devc, replays):
     cs = devc.cs
     res = {}
@@ -168,16 +172,25 @@ def latency_section(devc, replays):
         for label, use_ws in (("split", True), ("one_wg_per_question", False)):
             call, _ws = devc.call(w, q, c, out, use_workspace=use_ws)
             devc.time_calls(call, 50)
-            g_ms, nodes = devc.time_graph(call, replays)
-            d_ms = devc.time_calls(call, replays)
             st, grid, block, G = cs.cs_plan_launch(w.B, w.K, w.D, w.similarity, use_ws)
             assert st == 0
-            f_ms = devc.time_empty(grid, block, replays, True)
+            # five repetitions of replays/5 calls each; median (and min) per call
+            n = max(1, replays // LATENCY_REPS)
+            g, d, f = [], [], []
+            nodes = 0
+            for _ in range(LATENCY_REPS):
+                g_ms, nodes = devc.time_graph(call, n)
+                g.append(1e3 * g_ms / n)
+                d.append(1e3 * devc.time_calls(call, n) / n)
+                f.append(1e3 * devc.time_empty(grid, block, n, True) / n)
             row[label] = {"groups": G, "grid": grid, "block": block,
-                          "graph_us_per_call": round(1e3 * g_ms / replays, 3),
-                          "direct_us_per_call": round(1e3 * d_ms / replays, 3),
+                          "graph_us_per_call": round(float(np.median(g)), 3),
+                          "graph_us_per_call_min": round(min(g), 3),
+                          "direct_us_per_call": round(float(np.median(d)), 3),
+                          "direct_us_per_call_min": round(min(d), 3),
                           "graph_nodes": nodes,
-                          "empty_kernel_graph_floor_us": round(1e3 * f_ms / replays, 3)}
+                          "empty_kernel_graph_floor_us": round(float(np.median(f)), 3),
+                          "reps": LATENCY_REPS, "calls_per_rep": n}
         res[name] = row
         log(f"latency {name}: {row}")
         del q, c, out
