@@ -45,6 +45,9 @@ constexpr double kMinSplitBytes = 320.0 * 1024;
 // Ragged batches with more questions than this (about one per CU) are
 // dispatched longest-first.
 constexpr int kResidentQuestions = 256;
+// Longest-first scheduling: offsets bytes per workgroup at most 1/32 of a
+// mean question's candidate bytes.
+constexpr double kRankCostRatio = 32.0;
 // Candidate blocks larger than all eight XCD L2 caches together are streamed
 // with non-temporal loads.
 constexpr double kStreamBytes = 32.0 * 1024 * 1024;
@@ -256,8 +259,12 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   a.total_rows = total_rows;
   a.status = status;
   // More questions than resident workgroups (two 8-wave workgroups per CU):
-  // hand out the largest questions first so the batch ends evenly.
-  a.longest_first = B > kResidentQuestions ? 1 : 0;
+  // hand out the largest questions first so the batch ends evenly. Deriving
+  // that order costs every workgroup one pass over the B+1 offsets, so it is
+  // used only while that pass is small next to a question's own rows.
+  const double mean_question_bytes = 4.0 * (double)total_rows / (double)B * (double)D;
+  a.longest_first =
+      (B > kResidentQuestions && 8.0 * (double)B * kRankCostRatio <= mean_question_bytes) ? 1 : 0;
   // launch shape as for a dense batch of the same total size
   const int mean_k = (int)std::max<long long>(1, total_rows / B);
   cs::LaunchShape ls = make_shape(B, mean_k, D, 1, CS_MAX_K, Q, C);

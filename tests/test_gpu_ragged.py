@@ -46,7 +46,8 @@ def check(p, want, offsets, label):
 
 
 @pytest.mark.parametrize("B,D,sim", [(100, 512, "cosine"), (64, 2560, "dot"), (37, 1000, "cosine"),
-                                     (20, 3, "dot"), (300, 2560, "dot")])
+                                     (20, 3, "dot"), (300, 2560, "dot"),
+                                     (2000, 16, "cosine")])
 def test_ragged_matches_oracle(cs, orc, B, D, sim):
     offsets = workloads.ragged_offsets(41 + B, B)
     Q, C = workloads.ragged_inputs(43 + B, offsets, D)
