@@ -277,20 +277,28 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   return CS_OK;
 }
 
-// Projected-query workspace: q' [B][P] fp32; for dot also u [B][Hc] fp32
-// and the three-part bf16 split of q' [B][3 * P16] (P16 = P rounded up to 16).
+// Projected-query workspace: q' [B][P] fp32; for dot also u [B][Hc] fp32,
+// the three-part bf16 split of q' ([B rounded up to 32][3 * P16], P16 = P
+// rounded up to 16) and Wc^T ([Hc rounded up to 32][P16]), both bf16 in
+// matrix-core fragment order.
 size_t projected_qp_bytes(int B, int P) {
   return align_up(sizeof(float) * (size_t)B * (size_t)P, 256);
 }
 size_t projected_u_bytes(int B, int Hc) {
   return align_up(sizeof(float) * (size_t)B * (size_t)Hc, 256);
 }
+size_t projected_parts_bytes(int B, int P) {
+  const size_t p16 = (size_t)(P + 15) / 16 * 16, b32 = (size_t)(B + 31) / 32 * 32;
+  return align_up(sizeof(uint16_t) * b32 * 3 * p16, 256);
+}
+size_t projected_wpack_bytes(int Hc, int P) {
+  const size_t p16 = (size_t)(P + 15) / 16 * 16, h32 = (size_t)(Hc + 31) / 32 * 32;
+  return align_up(sizeof(uint16_t) * h32 * p16, 256);
+}
 size_t projected_workspace(int B, int Hc, int P, int sim) {
   size_t bytes = projected_qp_bytes(B, P);
-  if (sim == CS_SIM_DOT) {
-    const size_t p16 = (size_t)(P + 15) / 16 * 16;
-    bytes += projected_u_bytes(B, Hc) + sizeof(uint16_t) * (size_t)B * 3 * p16;
-  }
+  if (sim == CS_SIM_DOT)
+    bytes += projected_u_bytes(B, Hc) + projected_parts_bytes(B, P) + projected_wpack_bytes(Hc, P);
   return bytes;
 }
 
@@ -328,6 +336,8 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.u = reinterpret_cast<float*>(static_cast<char*>(ws) + projected_qp_bytes(B, P));
   p.parts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + projected_qp_bytes(B, P) +
                                         projected_u_bytes(B, Hc));
+  p.wpack = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(p.parts) +
+                                        projected_parts_bytes(B, P));
   p.B = B;
   p.K = K;
   p.Hq = Hq;

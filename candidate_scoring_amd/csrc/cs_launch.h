@@ -53,7 +53,8 @@ struct ProjArgs {
   float* out;          // [B][K]
   float* qp;           // workspace [B][P]: projected queries
   float* u;            // workspace [B][Hc]: folded queries (dot only)
-  uint16_t* parts;     // workspace [B][3 * P16]: bf16 split of q' (dot only)
+  uint16_t* parts;     // workspace: bf16 split of q', fragment-packed (dot only)
+  uint16_t* wpack;     // workspace: Wc^T, fragment-packed (dot only)
   int B, K, Hq, Hc, P;
   float zscale;        // scale / temperature
   int cosine;

@@ -111,6 +111,17 @@ __device__ __forceinline__ void lds_fragment(bf16x8_t& f, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
 
+// Fragment-packed operand of v_mfma_f32_32x32x16_bf16: element (row, k) of
+// an R x Kd matrix, with nks = Kd / 16 steps, sits in fragment (row / 32,
+// k / 16) at lane (row % 32) + 32 * ((k % 16) / 8), position k % 8; a
+// fragment is 64 lanes x 8 bf16 = 1 KiB, so one wave reads a whole fragment
+// with one contiguous 16-byte-per-lane load.
+__device__ __forceinline__ size_t frag_offset(long long row, int k, int nks) {
+  const long long rb = row / 32;
+  const int lane = (int)(row % 32) + 32 * ((k % 16) / 8);
+  return ((size_t)(rb * nks + k / 16) * kWave + lane) * 8 + (k % 8);
+}
+
 // x = hi + mid + lo exactly (bar underflow): each part is the bf16 rounding
 // of what the parts before it leave over; both residues are exact in fp32
 // and the last one has at most 8 significant bits. The parts are returned as
@@ -125,6 +136,44 @@ __device__ __forceinline__ float3 split3(float x) {
 // Bits of a float that bf16 represents exactly.
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return (uint16_t)(__float_as_uint(x) >> 16);
+}
+
+// W^T in fragment order for the fold: fragment (h / 32, p / 16) of the
+// H x P16 matrix w^T (zero past P and past H). A thread takes an 8 x 8 block
+// (rows p .. p+8, columns h .. h+8): eight 16-byte row loads (consecutive
+// threads read consecutive 16 bytes of a row), a transpose in registers, and
+// eight 16-byte stores, one per column h, which land in consecutive lanes of
+// one fragment.
+__global__ __launch_bounds__(256) void pack_wt_frags(const uint16_t* __restrict__ w,
+                                                     uint16_t* __restrict__ wp, int H, int P) {
+  const int p16 = (P + 15) / 16 * 16, nks = p16 / 16;
+  const int hg8 = (H + 31) / 32 * 4;  // 8-column groups, padded to whole fragments
+  const long long total = (long long)hg8 * (p16 / 8);
+  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int hgrp = (int)(t % hg8), pgrp = (int)(t / hg8);
+    const int h0 = 8 * hgrp, p0 = 8 * pgrp;
+    uint4 v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      v[r] = (p0 + r < P && h0 < H)
+                 ? *reinterpret_cast<const uint4*>(w + (size_t)(p0 + r) * (size_t)H + h0)
+                 : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(v);  // vw[4r + c/2] = w[p0+r][h0+c]
+    const int ks = p0 / 16, half = (p0 % 16) / 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t e0 = vw[4 * (2 * j) + c / 2], e1 = vw[4 * (2 * j + 1) + c / 2];
+        o[j] = (c & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
+      }
+      const int h = h0 + c;
+      const size_t piece = ((size_t)(h / 32) * nks + ks) * kWave + (h % 32) + 32 * half;
+      *reinterpret_cast<uint4*>(wp + piece * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,153 +244,89 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     const long long b = b0 + 8 * (e / 4) + 4 * (l / 32) + (e % 4);
     const int pp = p0 + (l & 31);
     if (b < B && pp < P) q[(size_t)b * (size_t)P + pp] = v;
-    // For the fold: q' split exactly into three bf16 parts, row b of `parts`
-    // holding hi | mid | lo, each padded with zeros to a multiple of 16.
+    // For the fold: q' split exactly into three bf16 parts (hi | mid | lo
+    // along the contraction, each padded with zeros to a multiple of 16),
+    // stored as matrix-core fragments (see frag_offset).
     const int p16 = (P + 15) / 16 * 16;
     if (parts != nullptr && b < B && pp < p16) {
       float3 sp = make_float3(0.0f, 0.0f, 0.0f);
-      uint16_t* row = parts + (size_t)b * (size_t)(3 * p16);
       if (pp < P) sp = split3(v);
-      row[pp] = bf16_bits(sp.x);
-      row[p16 + pp] = bf16_bits(sp.y);
-      row[2 * p16 + pp] = bf16_bits(sp.z);
+      const int nks = 3 * p16 / 16;
+      parts[frag_offset(b, pp, nks)] = bf16_bits(sp.x);
+      parts[frag_offset(b, p16 + pp, nks)] = bf16_bits(sp.y);
+      parts[frag_offset(b, 2 * p16 + pp, nks)] = bf16_bits(sp.z);
     }
   }
 }
 
 // u[b][h] = sum_p q'[b][p] * w[p][h]  (q' [B][P] fp32, w [P][H] bf16,
 // P <= 256, H % 8 == 0) on the bf16 matrix cores, from the three-part split
-// of q' that proj_query_mfma wrote (parts [B][3 * P16], P16 = P rounded up
-// to 16): the three products with a bf16 weight are exact and only the fp32
-// accumulation rounds, as in an fp32 dot product.
-//
-// Workgroup: 4 waves, 32 questions x 128 h; wave w takes columns
-// 32w .. +32. Both operands are staged in LDS first, with loads in which
-// consecutive lanes read consecutive bytes (a 16-byte-per-lane load that
-// touches 32 rows costs the L1 one tag lookup per row):
-//  * the questions' parts rows go in by DMA (global_load_lds_dwordx4), as
-//    blocks of 64 bf16 x 32 rows with the XOR swizzle of the ring kernel;
-//  * the contraction runs over p, the row index of w, so the 128 columns of
-//    w are staged transposed ([h][p], one 8 x 8 block of bf16 per thread,
-//    transposed in registers); weight fragments are then 16-byte reads.
-constexpr int kFoldRow = 256 + 8;              // bf16 per transposed row (p), padded
-constexpr int kFoldBlocks = 3 * 256 / 64;      // 64-wide blocks of a parts row, at most
-__shared__ __attribute__((aligned(1024))) uint8_t g_fold_a[kFoldBlocks][32 * 128];
+// of q' that proj_query_mfma wrote (hi | mid | lo along the contraction):
+// the three products with a bf16 weight are exact and only the fp32
+// accumulation rounds, as in an fp32 dot product. Both operands come
+// fragment-packed (parts by proj_query_mfma, w^T by pack_wt_frags), so every
+// operand load is one contiguous 1 KiB per wave and no LDS is involved. A
+// wave computes 32 questions x 128 h (four accumulators); per 16-wide step
+// over p it loads three part fragments and four weight fragments and issues
+// twelve matrix instructions, with the next step's loads in flight.
+constexpr int kFoldNb = 4;  // 32-column blocks per wave
 
 __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restrict__ parts,
-                                                       const uint16_t* __restrict__ w,
+                                                       const uint16_t* __restrict__ wp,
                                                        float* __restrict__ u, int B, int H,
                                                        int P) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[128 * kFoldRow];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int htiles = (H + 127) / 128;
-  const long long b0 = (long long)(blockIdx.x / htiles) * 32;
-  const int h0 = (int)(blockIdx.x % htiles) * 128;
-  const int p16 = (P + 15) / 16 * 16;
-  const int kq = 3 * p16;                       // bf16 per parts row
-  const int nblk = (kq + 63) / 64;
-  // Weight loads first (their registers are waited on before the transposed
-  // stores; the DMAs issued after them stay in flight).
-  // Task (pg, hg) moves w[8pg .. +8][h0 + 8hg .. +8] to wt[8hg .. +8][8pg .. +8].
-  // In a wave, 8 lanes take consecutive hg (128 contiguous bytes of a row)
-  // and 8 take consecutive pg; rows of w past P and columns past H are zero.
-  const int npg = p16 / 8;
-  constexpr int kTasks = 2;  // per thread: 32 pg x 16 hg at P16 = 256
-  uint4 v[kTasks][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long wid = (long long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int hgroups = (H + 32 * kFoldNb - 1) / (32 * kFoldNb);
+  const long long qb = wid / hgroups;
+  const int hg = (int)(wid % hgroups);
+  if (qb * 32 >= B) return;  // uniform across the wave
+  const int sp = (P + 15) / 16;           // 16-wide steps over p
+  const int hblocks = (H + 31) / 32;
+  const uint4* ap = reinterpret_cast<const uint4*>(parts) + (size_t)qb * (3 * sp) * kWave + lane;
+  const uint4* bp = reinterpret_cast<const uint4*>(wp) + lane;
+  f32x16_t acc[kFoldNb];
 #pragma unroll
-  for (int i = 0; i < kTasks; ++i) {
-    const int t = tid + 256 * i, blk = t / 64, tl = t % 64;
-    const int hg = 8 * (blk & 1) + (tl & 7), pg = 8 * (blk >> 1) + (tl >> 3);
-    const int hh = h0 + 8 * hg;
+  for (int nb = 0; nb < kFoldNb; ++nb)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int pr = 8 * pg + r;
-      v[i][r] = (pg < npg && pr < P && hh < H)
-                    ? *reinterpret_cast<const uint4*>(w + (size_t)pr * (size_t)H + hh)
-                    : make_uint4(0u, 0u, 0u, 0u);
+    for (int e = 0; e < 16; ++e) acc[nb][e] = 0.0f;
+  auto load = [&](int ks, uint4 (&a)[3], uint4 (&w)[kFoldNb]) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a[c] = ap[(size_t)(c * sp + ks) * kWave];
+#pragma unroll
+    for (int nb = 0; nb < kFoldNb; ++nb) {
+      const int hb = min(hg * kFoldNb + nb, hblocks - 1);
+      w[nb] = bp[((size_t)hb * sp + ks) * kWave];
     }
-  }
-  // Parts DMA: block kb, rows 8j .. +8 of the 32; wave w issues blocks
-  // w, w+4, ... (each 4 instructions). Lane l fills position l % 8 of row
-  // 8j + l / 8 with logical piece swizzled_piece(row, l % 8).
-  for (int kb = wave; kb < nblk; kb += 4) {
+  };
+  uint4 a[2][3], w[2][kFoldNb];
+  load(0, a[0], w[0]);
+  for (int ks = 0; ks < sp; ks += 2) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 8 * j + lane / 8;
-      const int k = 64 * kb + 8 * swizzled_piece(row, lane % 8);
-      const uint16_t* src = parts + (size_t)min(b0 + row, (long long)B - 1) * (size_t)kq +
-                            (k < kq ? k : 0);
-      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(g_fold_a[kb] + 1024 * j), 16,
-                                       0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kTasks; ++i) {
-    const int t = tid + 256 * i, blk = t / 64, tl = t % 64;
-    const int hg = 8 * (blk & 1) + (tl & 7), pg = 8 * (blk >> 1) + (tl >> 3);
-    if (pg >= npg) continue;
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(v[i]);  // vw[4r + c/2] = w[r][c]
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t o[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t e0 = vw[4 * (2 * jj) + c / 2], e1 = vw[4 * (2 * jj + 1) + c / 2];
-        o[jj] = (c & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
-      }
-      *reinterpret_cast<uint4*>(&wt[(8 * hg + c) * kFoldRow + 8 * pg]) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-  const int r = lane & 31, half = lane >> 5;
-  const uint32_t abase = lds_address(g_fold_a[0]);
-  const uint16_t* wrow = &wt[(32 * wave + r) * kFoldRow + 8 * half];
-  // One accumulator per part, so the three products of a step are
-  // independent and share the weight fragment. Every lane runs the same steps
-  // (the matrix instructions need the whole wave); in step s, lane half h
-  // feeds features 16s + 8h .. +8, which sit at k = c * P16 + 16s + 8h of
-  // the parts row for part c. Four steps' reads are issued before one wait.
-  f32x16_t acc[3];
-#pragma unroll
-  for (int c = 0; c < 3; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
-  for (int kb0 = 0; kb0 < p16; kb0 += 64) {
-    bf16x8_t af[4][3], wf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k0 = kb0 + 16 * j;
-      if (k0 < p16) {  // uniform
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-          const int k = c * p16 + k0 + 8 * half;
-          lds_fragment<0>(af[j][c], abase + (uint32_t)((k / 64) * (32 * 128) + r * 128 +
-                                                       16 * swizzled_piece(r, (k % 64) / 8)));
-        }
-        lds_fragment<0>(wf[j], lds_address(reinterpret_cast<const uint8_t*>(wrow + k0)));
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kb0 + 16 * j < p16) {
-        asm volatile("" : "+v"(af[j][0]), "+v"(af[j][1]), "+v"(af[j][2]), "+v"(wf[j]));
+    for (int i = 0; i < 2; ++i) {
+      if (ks + i < sp) {  // uniform
+        if (ks + i + 1 < sp) load(ks + i + 1, a[i ^ 1], w[i ^ 1]);
 #pragma unroll
         for (int c = 0; c < 3; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j][c], wf[j], acc[c], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < kFoldNb; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, a[i][c]), __builtin_bit_cast(bf16x8_t, w[i][nb]),
+                acc[nb], 0, 0, 0);
       }
     }
   }
-  // Accumulator e of lane l: question b0 + 8*(e/4) + 4*(l/32) + e%4, column
-  // h0 + 32*wave + l%32.
-  const int hcol = h0 + 32 * wave + (lane & 31);
-  if (hcol >= H) return;
+  // Accumulator e of lane l: question 32*qb + 8*(e/4) + 4*(l/32) + e%4,
+  // column 32*(hg*4 + nb) + l%32.
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const long long b = b0 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
-    if (b < B) u[(size_t)b * (size_t)H + hcol] = acc[0][e] + (acc[1][e] + acc[2][e]);
+  for (int nb = 0; nb < kFoldNb; ++nb) {
+    const int hcol = 32 * (hg * kFoldNb + nb) + (lane & 31);
+    if (hcol >= H) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const long long b = qb * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+      if (b < B) u[(size_t)b * (size_t)H + hcol] = acc[nb][e];
+    }
   }
 }
 
@@ -969,12 +954,16 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.zscale = p.zscale;
   a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
-  // u = Wc^T q' (one workgroup per 32 questions x 128 h), then one
-  // bandwidth-bound pass over the candidates.
+  // W^T in fragment order, then u = Wc^T q' (one wave per 32 questions x
+  // 128 h), then one bandwidth-bound pass over the candidates.
   {
-    const long long groups = (long long)((p.B + 31) / 32) * ((p.Hc + 127) / 128);
-    hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)groups), dim3(256), 0, stream, p.parts,
-                       p.wc, p.u, p.B, p.Hc, p.P);
+    const long long blocks = (long long)((p.Hc + 31) / 32 * 4) * ((p.P + 15) / 16 * 2);
+    hipLaunchKernelGGL(pack_wt_frags, dim3((unsigned)std::min<long long>((blocks + 255) / 256, 4096)),
+                       dim3(256), 0, stream, p.wc, p.wpack, p.Hc, p.P);
+    const long long waves =
+        (long long)((p.B + 31) / 32) * ((p.Hc + 32 * kFoldNb - 1) / (32 * kFoldNb));
+    hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                       p.parts, p.wpack, p.u, p.B, p.Hc, p.P);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -172,11 +172,12 @@ int cs_score_candidates_ragged(const float *queries, const float *candidates,
  * for cosine, each question's projected candidates are computed on the
  * matrix cores and reduced to their similarity in registers. The workspace
  * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected
- * queries and, for dot, the folded queries and an exact three-part bf16
- * split of the projected ones. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
+ * queries and, for dot, the folded queries, an exact three-part bf16 split
+ * of the projected ones and Wc^T, both in matrix-core fragment order; its
+ * contents are scratch between calls. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
  * 16-byte aligned inputs, P a multiple of 64 for cosine, Hc <= 4096 for dot;
  * other valid sizes return CS_ERR_UNSUPPORTED. Enqueues two (cosine) or
- * three (dot) kernels on `stream`. */
+ * four (dot) kernels on `stream`. */
 size_t cs_projected_workspace_bytes(int B, int Hc, int P, int similarity);
 int cs_score_projected(const uint16_t *xq, const uint16_t *xc, const uint16_t *wq,
                        const uint16_t *wc, int B, int K, int Hq, int Hc, int P, int similarity,
