@@ -139,40 +139,41 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 }
 
 // W^T in fragment order for the fold: fragment (h / 32, p / 16) of the
-// H x P16 matrix w^T (zero past P and past H). A thread takes an 8 x 8 block
-// (rows p .. p+8, columns h .. h+8): eight 16-byte row loads (consecutive
-// threads read consecutive 16 bytes of a row), a transpose in registers, and
-// eight 16-byte stores, one per column h, which land in consecutive lanes of
-// one fragment.
-__global__ __launch_bounds__(256) void pack_wt_frags(const uint16_t* __restrict__ w,
-                                                     uint16_t* __restrict__ wp, int H, int P) {
-  const int p16 = (P + 15) / 16 * 16, nks = p16 / 16;
-  const int hg8 = (H + 31) / 32 * 4;  // 8-column groups, padded to whole fragments
-  const long long total = (long long)hg8 * (p16 / 8);
-  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (long long)gridDim.x * blockDim.x) {
-    const int hgrp = (int)(t % hg8), pgrp = (int)(t / hg8);
-    const int h0 = 8 * hgrp, p0 = 8 * pgrp;
-    uint4 v[8];
+// H x P16 matrix w^T (zero past P and past H), in 8 x 8 blocks (rows
+// p .. p+8, columns h .. h+8; the 8-column groups are padded to whole
+// fragments). Block t: eight 16-byte row loads (consecutive blocks read
+// consecutive 16 bytes of a row), a transpose in registers, and eight 16-byte
+// stores, one per column h, which land in consecutive lanes of one fragment.
+__host__ __device__ inline long long pack_wt_blocks(int H, int P) {
+  return (long long)((H + 31) / 32 * 4) * ((P + 15) / 16 * 2);
+}
+
+__device__ __forceinline__ void pack_wt_block(const uint16_t* __restrict__ w,
+                                              uint16_t* __restrict__ wp, int H, int P,
+                                              long long t) {
+  const int nks = (P + 15) / 16;
+  const int hg8 = (H + 31) / 32 * 4;
+  const int hgrp = (int)(t % hg8), pgrp = (int)(t / hg8);
+  const int h0 = 8 * hgrp, p0 = 8 * pgrp;
+  uint4 v[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      v[r] = (p0 + r < P && h0 < H)
-                 ? *reinterpret_cast<const uint4*>(w + (size_t)(p0 + r) * (size_t)H + h0)
-                 : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(v);  // vw[4r + c/2] = w[p0+r][h0+c]
-    const int ks = p0 / 16, half = (p0 % 16) / 8;
+  for (int r = 0; r < 8; ++r)
+    v[r] = (p0 + r < P && h0 < H)
+               ? *reinterpret_cast<const uint4*>(w + (size_t)(p0 + r) * (size_t)H + h0)
+               : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(v);  // vw[4r + c/2] = w[p0+r][h0+c]
+  const int ks = p0 / 16, half = (p0 % 16) / 8;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t o[4];
+  for (int c = 0; c < 8; ++c) {
+    uint32_t o[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t e0 = vw[4 * (2 * j) + c / 2], e1 = vw[4 * (2 * j + 1) + c / 2];
-        o[j] = (c & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
-      }
-      const int h = h0 + c;
-      const size_t piece = ((size_t)(h / 32) * nks + ks) * kWave + (h % 32) + 32 * half;
-      *reinterpret_cast<uint4*>(wp + piece * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e0 = vw[4 * (2 * j) + c / 2], e1 = vw[4 * (2 * j + 1) + c / 2];
+      o[j] = (c & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
     }
+    const int h = h0 + c;
+    const size_t piece = ((size_t)(h / 32) * nks + ks) * kWave + (h % 32) + 32 * half;
+    *reinterpret_cast<uint4*>(wp + piece * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -193,12 +194,27 @@ constexpr int kPqDepth = 2;  // blocks in flight per wave
 
 __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ q,
-    uint16_t* __restrict__ parts, int B, int H, int P) {
+    uint16_t* __restrict__ parts, int B, int H, int P, const uint16_t* __restrict__ wc,
+    uint16_t* __restrict__ wpack, int Hc) {
   __shared__ float part[kPqWaves][16][kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (wpack != nullptr) {
+    // This workgroup's share of the fold's W^T packing (independent of q').
+    const long long total = pack_wt_blocks(Hc, P);
+    const long long per = (total + gridDim.x - 1) / gridDim.x;
+    const long long end = min(total, per * ((long long)blockIdx.x + 1));
+    for (long long t = per * blockIdx.x + tid; t < end; t += blockDim.x)
+      pack_wt_block(wc, wpack, Hc, P, t);
+  }
   const int ptiles = (P + 31) / 32;
-  const long long b0 = (long long)(blockIdx.x / ptiles) * 32;
-  const int p0 = (int)(blockIdx.x % ptiles) * 32;
+  // Consecutive workgroups go to different XCDs (each with its own L2), so
+  // when the grid divides evenly, XCD j is given tiles j*(grid/8) ..: the
+  // tiles of a few question blocks, which then read their rows of x from
+  // one L2 instead of every XCD reading all of x.
+  long long tile = blockIdx.x;
+  if (gridDim.x % 8 == 0) tile = (long long)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const long long b0 = (tile / ptiles) * 32;
+  const int p0 = (int)(tile % ptiles) * 32;
   const int r = lane & 31, half = lane >> 5;
   const uint16_t* xr = x + (size_t)min(b0 + r, (long long)B - 1) * (size_t)H;
   const uint16_t* wr = w + (size_t)min(p0 + r, P - 1) * (size_t)H;
@@ -264,7 +280,7 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
 // of q' that proj_query_mfma wrote (hi | mid | lo along the contraction):
 // the three products with a bf16 weight are exact and only the fp32
 // accumulation rounds, as in an fp32 dot product. Both operands come
-// fragment-packed (parts by proj_query_mfma, w^T by pack_wt_frags), so every
+// fragment-packed (parts and w^T by proj_query_mfma), so every
 // operand load is one contiguous 1 KiB per wave and no LDS is involved. A
 // wave computes 32 questions x 128 h (four accumulators); per 16-wide step
 // over p it loads three part fragments and four weight fragments and issues
@@ -939,8 +955,10 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
   {
     const long long groups = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
+    // For dot the same launch also packs Wc^T for the fold.
     hipLaunchKernelGGL(proj_query_mfma, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream,
-                       p.xq, p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P);
+                       p.xq, p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P, p.wc,
+                       p.cosine ? nullptr : p.wpack, p.Hc);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -954,12 +972,9 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.zscale = p.zscale;
   a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
-  // W^T in fragment order, then u = Wc^T q' (one wave per 32 questions x
-  // 128 h), then one bandwidth-bound pass over the candidates.
+  // u = Wc^T q' (one wave per 32 questions x 128 h), then one
+  // bandwidth-bound pass over the candidates.
   {
-    const long long blocks = (long long)((p.Hc + 31) / 32 * 4) * ((p.P + 15) / 16 * 2);
-    hipLaunchKernelGGL(pack_wt_frags, dim3((unsigned)std::min<long long>((blocks + 255) / 256, 4096)),
-                       dim3(256), 0, stream, p.wc, p.wpack, p.Hc, p.P);
     const long long waves =
         (long long)((p.B + 31) / 32) * ((p.Hc + 32 * kFoldNb - 1) / (32 * kFoldNb));
     hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,

@@ -177,7 +177,7 @@ int cs_score_candidates_ragged(const float *queries, const float *candidates,
  * contents are scratch between calls. Implemented shapes: Hq and Hc multiples of 8, P <= 256,
  * 16-byte aligned inputs, P a multiple of 64 for cosine, Hc <= 4096 for dot;
  * other valid sizes return CS_ERR_UNSUPPORTED. Enqueues two (cosine) or
- * four (dot) kernels on `stream`. */
+ * three (dot) kernels on `stream`. */
 size_t cs_projected_workspace_bytes(int B, int Hc, int P, int similarity);
 int cs_score_projected(const uint16_t *xq, const uint16_t *xc, const uint16_t *wq,
                        const uint16_t *wc, int B, int K, int Hq, int Hc, int P, int similarity,
