@@ -9,6 +9,7 @@ include/candidate_scoring.h) and ``candidate_scoring_amd/libcs_bench.so``
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,24 +46,61 @@ def common_flags() -> list[str]:
     ]
 
 
-def _run(cmd: list[str], verbose: bool) -> None:
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _run(cmd: list[str], verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    lines = [l for l in res.stderr.splitlines() if noise not in l]
+    err = "\n".join(l for l in lines if RESOURCE_REMARKS not in l)
     if res.returncode != 0:
         raise RuntimeError(f"build failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    return "\n".join(lines)
+
+
+def spilling_kernels(remarks: str) -> list[tuple[str, int]]:
+    """Kernels whose resource-usage remarks report scratch (spilled) memory.
+
+    The fragment reads of the matrix-core kernels are inline ds_read
+    instructions that the compiler does not track: a value it spilled or
+    copied between such a read and its explicit wait would be taken before
+    the data arrived. Every kernel of the library is therefore required to
+    run without scratch, and the build checks it.
+    """
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None:
+            if int(m.group(1)) > 0:
+                out.append((name, int(m.group(1))))
+            name = None
+    return out
 
 
 def build(verbose: bool = False) -> list[Path]:
     cc = hipcc()
     tmp = LIBRARY.with_suffix(".so.tmp")
-    _run([cc, *common_flags(), "-o", str(tmp), str(CSRC / "cs_kernels.hip"),
-          str(CSRC / "cs_project.hip"), str(CSRC / "cs_api.cpp")], verbose)
+    remarks = _run([cc, *common_flags(), RESOURCE_REMARKS, "-fno-caret-diagnostics", "-o", str(tmp),
+                    str(CSRC / "cs_kernels.hip"), str(CSRC / "cs_project.hip"),
+                    str(CSRC / "cs_api.cpp")], verbose)
+    if "ScratchSize" not in remarks:
+        raise RuntimeError("build: the compiler printed no kernel resource usage to check")
+    spills = spilling_kernels(remarks)
+    if spills:
+        tmp.unlink(missing_ok=True)
+        raise RuntimeError("build: kernels use scratch memory (spills), which the untracked "
+                           "fragment reads do not allow: " + ", ".join(f"{n} ({b} B/lane)"
+                                                                     for n, b in spills))
     tmp.replace(LIBRARY)
     tmpb = BENCH_LIBRARY.with_suffix(".so.tmp")
     _run([cc, *common_flags(), "-o", str(tmpb), str(CSRC / "cs_bench.hip"),
