@@ -34,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 halves of a 32-bit word, widened exactly to fp32.
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -183,12 +184,10 @@ __device__ __forceinline__ void pack_wt_block(const uint16_t* __restrict__ w,
 // hidden sum is split over the waves in 64-wide blocks (wave w takes blocks
 // w, w+16, ...), and a wave issues the loads of two blocks before
 // its first multiply, so the tile's operands are in flight at once. Both
-// operands come straight from global memory: in a block, lane l takes row
-// l % 32 and the 32 consecutive hidden elements 32*(l/32) .. +32, four
-// 16-byte pieces, and piece j of both operands feeds the j-th
-// v_mfma_f32_32x32x16_bf16 -- the same hidden indices pair up on both sides,
-// which is all a contraction needs. bf16 products are exact in fp32; the 16
-// partial tiles are added in wave order through LDS.
+// operands come straight from global memory as v_mfma_f32_16x16x32_bf16
+// fragments (the same hidden indices pair up on both sides, which is all a
+// contraction needs). bf16 products are exact in fp32; the 16 partial tiles
+// are added in wave order through LDS.
 constexpr int kPqWaves = 16;
 constexpr int kPqDepth = 2;  // blocks in flight per wave
 
@@ -215,29 +214,46 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
   if (gridDim.x % 8 == 0) tile = (long long)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   const long long b0 = (tile / ptiles) * 32;
   const int p0 = (int)(tile % ptiles) * 32;
-  const int r = lane & 31, half = lane >> 5;
-  const uint16_t* xr = x + (size_t)min(b0 + r, (long long)B - 1) * (size_t)H;
-  const uint16_t* wr = w + (size_t)min(p0 + r, P - 1) * (size_t)H;
-  f32x16_t acc;
+  // v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of a 16-row block and
+  // hidden elements 8*(l/16) .. +8 of a 32-wide step, so the four lanes of a
+  // row read 64 contiguous bytes and one 16-byte-per-lane load touches 16
+  // rows (with 32x32x16 fragments it touched 32, each row's cache line looked
+  // up once per 32 bytes). A workgroup's 32 x 32 tile is 2 x 2 such blocks.
+  const int r16 = lane & 15, kq = lane >> 4;
+  const uint16_t* xr[2];
+  const uint16_t* wr[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int h = 0; h < 2; ++h) {
+    xr[h] = x + (size_t)min(b0 + 16 * h + r16, (long long)B - 1) * (size_t)H;
+    wr[h] = w + (size_t)min(p0 + 16 * h + r16, P - 1) * (size_t)H;
+  }
+  f32x4_t acc4[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc4[rb][cb][i] = 0.0f;
   const int nblk = (H + 63) / 64;
   for (int kb0 = wave; kb0 < nblk; kb0 += kPqDepth * kPqWaves) {
-    bf16x8_t av[kPqDepth][4], wv[kPqDepth][4];
+    bf16x8_t av[kPqDepth][2][2], wv[kPqDepth][2][2];  // [block][row half][k-step]
 #pragma unroll
     for (int d = 0; d < kPqDepth; ++d) {
       const int kb = kb0 + d * kPqWaves;
-      const int k = 64 * kb + 32 * half;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (kb < nblk && k + 8 * j < H) {
-          av[d][j] = *reinterpret_cast<const bf16x8_t*>(xr + k + 8 * j);
-          wv[d][j] = *reinterpret_cast<const bf16x8_t*>(wr + k + 8 * j);
-        } else {
+      for (int st = 0; st < 2; ++st) {
+        const int k = 64 * kb + 32 * st + 8 * kq;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            av[d][j][e] = (__bf16)0.0f;
-            wv[d][j][e] = (__bf16)0.0f;
+        for (int h = 0; h < 2; ++h) {
+          if (kb < nblk && k < H) {
+            av[d][h][st] = *reinterpret_cast<const bf16x8_t*>(xr[h] + k);
+            wv[d][h][st] = *reinterpret_cast<const bf16x8_t*>(wr[h] + k);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              av[d][h][st][e] = (__bf16)0.0f;
+              wv[d][h][st][e] = (__bf16)0.0f;
+            }
           }
         }
       }
@@ -245,24 +261,31 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
 #pragma unroll
     for (int d = 0; d < kPqDepth; ++d)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[d][j], wv[d][j], acc, 0, 0, 0);
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d][rb][st], wv[d][cb][st],
+                                                                   acc4[rb][cb], 0, 0, 0);
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) part[wave][e][lane] = acc[e];
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave][4 * (2 * rb + cb) + i][lane] = acc4[rb][cb][i];
   __syncthreads();
-  // Accumulator e of lane l is q'[b0 + 8*(e/4) + 4*(l/32) + e%4][p0 + l%32].
+  // Element i of tile (rb, cb) in lane l is q'[b0 + 16*rb + 4*(l/16) + i][p0 + 16*cb + l%16].
   {
     const int e = tid / kWave, l = tid % kWave;  // 1024 threads, 16 x 64 outputs
     float v = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][l];
-    const long long b = b0 + 8 * (e / 4) + 4 * (l / 32) + (e % 4);
-    const int pp = p0 + (l & 31);
+    const int t = e / 4, i = e % 4, rb = t / 2, cb = t % 2;
+    const long long b = b0 + 16 * rb + 4 * (l / 16) + i;
+    const int pp = p0 + 16 * cb + (l & 15);
     if (b < B && pp < P) q[(size_t)b * (size_t)P + pp] = v;
-    // For the fold: q' split exactly into three bf16 parts (hi | mid | lo
-    // along the contraction, each padded with zeros to a multiple of 16),
-    // stored as matrix-core fragments (see frag_offset).
     const int p16 = (P + 15) / 16 * 16;
     if (parts != nullptr && b < B && pp < p16) {
       float3 sp = make_float3(0.0f, 0.0f, 0.0f);
