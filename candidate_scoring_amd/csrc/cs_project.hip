@@ -315,7 +315,11 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
                                                        float* __restrict__ u, int B, int H,
                                                        int P) {
   const int lane = threadIdx.x & (kWave - 1);
-  const long long wid = (long long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  // Workgroups numbered per XCD, as in proj_query_mfma: XCD j takes a run of
+  // question blocks and reads only their parts from its own L2.
+  long long wg = blockIdx.x;
+  if (gridDim.x % 8 == 0) wg = (long long)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const long long wid = wg * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int hgroups = (H + 32 * kFoldNb - 1) / (32 * kFoldNb);
   const long long qb = wid / hgroups;
   const int hg = (int)(wid % hgroups);
