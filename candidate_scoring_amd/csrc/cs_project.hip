@@ -639,21 +639,30 @@ __device__ __forceinline__ void stage_barrier() {
 // row K-1 and W rows past P repeat row P-1; those rows are never read. (The
 // helpers take plain pointers: restrict-qualified parameters of an inlined
 // function would give every call site alias scopes of its own.)
+// DMA of hidden chunk c into stage S: this wave fills rows RPW*wave .. +RPW
+// of the X tile and of the W tile. X rows past K repeat row K-1 and W rows
+// past P repeat row P-1; those rows are never read. The per-lane offsets
+// (32-bit: the host keeps K*H*2 below 2^31) are recomputed for every fill
+// from an opaque copy of the lane index, so the compiler cannot hoist them
+// out of the chunk loop and hold them in registers beside the accumulators.
 template <int S, int RPW, bool NT>
 __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* wc, int c, int K,
                                            int P, int H, int wave, int lane) {
-  const int h0 = c * kAChunk;
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(Xb) + (size_t)c * kARowBytes;
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wc) + (size_t)c * kARowBytes;
 #pragma unroll
   for (int j = 0; j < RPW / kARowsPerLoad; ++j) {
     const int r0 = RPW * wave + kARowsPerLoad * j;
-    const int row = r0 + lane / kAPieces;
-    const int piece = swizzled_piece(row, lane % kAPieces);
-    const uint16_t* src = Xb + (size_t)min(row, K - 1) * (size_t)H + h0 + 8 * piece;
-    __builtin_amdgcn_global_load_lds((global_ptr_t)src,
+    const int row = r0 + ln / kAPieces;
+    const int piece = swizzled_piece(row, ln % kAPieces);
+    const uint32_t xo = (uint32_t)(2 * (min(row, K - 1) * H + 8 * piece));
+    const uint32_t wo = (uint32_t)(2 * (min(row, P - 1) * H + 8 * piece));
+    __builtin_amdgcn_global_load_lds((global_ptr_t)(xb + xo),
                                      (lds_ptr_t)(stage_tile<S, false>() + r0 * kARowBytes), 16, 0,
                                      NT ? 2 : 0);
-    const uint16_t* wsrc = wc + (size_t)min(row, P - 1) * (size_t)H + h0 + 8 * piece;
-    __builtin_amdgcn_global_load_lds((global_ptr_t)wsrc,
+    __builtin_amdgcn_global_load_lds((global_ptr_t)(wb + wo),
                                      (lds_ptr_t)(stage_tile<S, true>() + r0 * kARowBytes), 16, 0,
                                      0);
   }
@@ -737,12 +746,13 @@ __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[RB][TN], const StageO
 // c+1, multiply chunk c. Chunk c+1 may be the first of the next question of
 // this workgroup (Xn; null when there is none or when questions do not carry
 // the ring). The step with c < 0 only fills (the start of the ring).
+constexpr int kDmaWaves = 4;
+
 template <int S, int TN, int RB, bool NT>
 __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageOffsets& o,
                                            const uint16_t* Xb, const uint16_t* Xn,
                                            const uint16_t* wc, int c, int nchunks, int K, int H,
                                            int wave, int lane) {
-  constexpr int kWaves = 16 / RB;  // 4 x 2 (RB = 2) or 2 x 2 (RB = 4) tiles of the output
   if (c >= nchunks) return;
   if (c >= 0) {
     // With two stages the only chunk in flight is c itself (issued at the
@@ -756,9 +766,13 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageO
     next -= nchunks;
     src = Xn;
   }
-  if (next >= 0 && src != nullptr)
-    stage_fill<(S + kAStages - 1) % kAStages, 256 / kWaves, NT>(src, wc, next, K, 64 * TN, H,
-                                                                wave, lane);
+  // Waves 0 .. 3 (one per SIMD) issue the chunk's DMAs, 64 rows each; the
+  // other wave of each SIMD goes straight to its matrix work, so the SIMD's
+  // matrix core is not idle while the DMA instructions queue for the memory
+  // pipeline (all eight waves issuing measured 3-5 % slower).
+  if (next >= 0 && src != nullptr && wave < kDmaWaves)
+    stage_fill<(S + kAStages - 1) % kAStages, 256 / kDmaWaves, NT>(src, wc, next, K, 64 * TN, H,
+                                                                   wave, lane);
   if (c >= 0) stage_mfma<S, TN, RB>(acc, o);
 }
 
@@ -944,7 +958,8 @@ constexpr int kCosRowBlocks = 2;
 
 template <int TN, bool NT>
 void launch_cos_tile(const KernelArgs& a, const ProjArgs& p, unsigned grid, hipStream_t stream) {
-  if (p.Hc % kAChunk == 0)
+  // The ring's DMA offsets are 32-bit byte offsets into a question's rows.
+  if (p.Hc % kAChunk == 0 && 2LL * p.K * p.Hc < (1LL << 31))
     // One resident workgroup per compute unit (its LDS allows no more), each
     // working through its share of the questions.
     hipLaunchKernelGGL((proj_cos_mfma_async<TN, NT, kCosRowBlocks>),
