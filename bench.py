@@ -512,7 +512,8 @@ def main():
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)
-        # the box's share of host cores is 16, whatever the machine reports
+        # at most 16 host threads: a process sharing its machine may be
+        # allotted fewer cores than os.cpu_count() reports
         threads = max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"]["threaded"] = cpu_baseline_threaded(w, threads)
     print(json.dumps(result), flush=True)
