@@ -6,8 +6,9 @@ the HIP kernels. Pointer arguments accept a torch tensor on a HIP device, a
 raw integer device address, or None (NULL). ``stream`` accepts None (torch's
 current stream), a ``torch.cuda.Stream`` or a raw ``hipStream_t`` integer.
 
-``score`` is a convenience wrapper that allocates the output (and a cached
-workspace) with torch and raises on a non-OK status.
+``score``, ``score_ragged`` and ``score_projected`` are convenience wrappers
+that allocate the output (and a cached workspace) with torch and raise on a
+non-OK status.
 
 There is no fallback: if the library is not built, ``load`` raises.
 """
@@ -251,18 +252,20 @@ def cs_score_projected(xq, xc, wq, wc, B: int, K: int, Hq: int, Hc: int, P: int,
 
 
 # ----------------------------------------------------------------------------
-# Convenience wrapper.
+# Convenience wrappers.
 
 _workspaces: dict = {}
 
 
-def workspace(nbytes: int, device=None, stream=None):
-    """A zeroed workspace of at least ``nbytes`` cached per (device, stream).
-    Calls that may overlap must not share one, hence the per-stream key."""
+def workspace(nbytes: int, device=None, stream=None, kind: str = "split"):
+    """A zeroed workspace of at least ``nbytes`` cached per (device, stream,
+    kind). Calls that may overlap must not share one, hence the per-stream
+    key; the split path's workspace must stay zeroed between calls while the
+    projection's is scratch, hence the kind."""
     import torch
 
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-    key = (str(device), _stream(stream))
+    key = (str(device), _stream(stream), kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -306,6 +309,60 @@ def score(query, candidates, similarity="cosine", scale=1.0, temperature=1.0, ou
     else:
         st = cs_score_candidates_batch(query, candidates, B, K, D, sim, scale, temperature,
                                        out, ws, nbytes, stream)
+    if st != CS_OK:
+        raise ScoringError(st)
+    return out
+
+
+def score_ragged(queries, candidates, offsets, similarity="cosine", scale=1.0,
+                 temperature=1.0, out=None, status=None, stream=None):
+    """Probabilities for a ragged batch: queries [B, D], candidates
+    [total_rows, D] packed by question, offsets int64 [B + 1] on the device
+    (question b owns rows offsets[b] .. offsets[b+1]-1, 1 to 255 of them).
+    Returns out [total_rows]. A question with bad offsets is skipped and, if
+    ``status`` (an int32 device tensor) is given, flagged there."""
+    import torch
+
+    B, D = queries.shape
+    total_rows = candidates.shape[0]
+    if candidates.dim() != 2 or candidates.shape[1] != D:
+        raise ValueError("candidates must be [total_rows, D]")
+    if offsets.dtype != torch.int64 or offsets.numel() != B + 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int64 tensor of B + 1 entries")
+    if out is None:
+        out = torch.empty(total_rows, dtype=torch.float32, device=candidates.device)
+    for t in (queries, candidates, out):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("fp32 contiguous tensors required")
+    st = cs_score_candidates_ragged(queries, candidates, offsets, B, total_rows, D, similarity,
+                                    scale, temperature, out, status, stream)
+    if st != CS_OK:
+        raise ScoringError(st)
+    return out
+
+
+def score_projected(xq, xc, wq, wc, similarity="cosine", scale=1.0, temperature=1.0, out=None,
+                    stream=None):
+    """Probabilities with the heads applied: hidden states xq [B, Hq] and
+    xc [B, K, Hc], heads wq [P, Hq] and wc [P, Hc], all bfloat16 contiguous
+    device tensors; q' = wq xq and c'_k = wc xc_k are scored as by score().
+    Returns out [B, K] (fp32)."""
+    import torch
+
+    B, Hq = xq.shape
+    B2, K, Hc = xc.shape
+    P = wq.shape[0]
+    if B2 != B or tuple(wq.shape) != (P, Hq) or tuple(wc.shape) != (P, Hc):
+        raise ValueError("shapes must be xq [B, Hq], xc [B, K, Hc], wq [P, Hq], wc [P, Hc]")
+    for t in (xq, xc, wq, wc):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("bfloat16 contiguous tensors required")
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.float32, device=xc.device)
+    nbytes = cs_projected_workspace_bytes(B, Hc, P, similarity)
+    ws = workspace(nbytes, xc.device, stream, kind="projected")
+    st = cs_score_projected(xq, xc, wq, wc, B, K, Hq, Hc, P, similarity, scale, temperature, out,
+                            ws, ws.numel(), stream)
     if st != CS_OK:
         raise ScoringError(st)
     return out

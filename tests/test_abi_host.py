@@ -256,3 +256,26 @@ def test_projected_rejections_before_device_work(lib):
     assert np.all(out == -7.0)
     assert cs.cs_projected_workspace_bytes(2, 64, 64, "dot") > cs.cs_projected_workspace_bytes(
         2, 64, 64, "cosine") > 0
+
+
+def test_wrappers_check_shapes_and_dtypes_first():
+    """score_ragged() and score_projected() refuse malformed arguments before
+    any call into the library (host tensors suffice to show it)."""
+    import torch
+
+    q, c = torch.zeros((2, 8)), torch.zeros((4, 8))
+    with pytest.raises(ValueError, match="B \\+ 1"):
+        cs.score_ragged(q, c, torch.tensor([0, 4], dtype=torch.int64))
+    with pytest.raises(ValueError, match="int64"):
+        cs.score_ragged(q, c, torch.tensor([0, 2, 4], dtype=torch.int32))
+    with pytest.raises(ValueError, match="total_rows"):
+        cs.score_ragged(q, torch.zeros((4, 9)), torch.tensor([0, 2, 4], dtype=torch.int64))
+    bf = torch.bfloat16
+    xq, xc = torch.zeros((2, 64), dtype=bf), torch.zeros((2, 5, 64), dtype=bf)
+    wq, wc = torch.zeros((64, 64), dtype=bf), torch.zeros((64, 64), dtype=bf)
+    with pytest.raises(ValueError, match="shapes"):
+        cs.score_projected(xq, xc[:1], wq, wc)
+    with pytest.raises(ValueError, match="shapes"):
+        cs.score_projected(xq, xc, wq, wc[:, :32])
+    with pytest.raises(ValueError, match="bfloat16"):
+        cs.score_projected(xq.float(), xc, wq, wc)
