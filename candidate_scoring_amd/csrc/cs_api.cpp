@@ -74,6 +74,9 @@ int validate(const void* q, const void* c, const void* out, long long B, long lo
   if (sim != CS_SIM_DOT && sim != CS_SIM_COSINE) return CS_ERR_SIMILARITY;
   if (scale == 0.0f || isnan(scale) || isinf(scale)) return CS_ERR_SCALE;
   if (!(temperature > 0.0f) || isinf(temperature)) return CS_ERR_TEMPERATURE;
+  // The kernels form every logit with the factor scale / T rounded once to
+  // fp32; a quotient beyond the fp32 range would make every logit infinite.
+  if (isinf((float)((double)scale / (double)temperature))) return CS_ERR_SCALE;
   return CS_OK;
 }
 
@@ -367,7 +370,8 @@ const char* cs_status_string(int status) {
     case CS_ERR_NULL_POINTER: return "null query, candidates or output pointer";
     case CS_ERR_K_RANGE: return "candidate count K must be in 1..255";
     case CS_ERR_D_RANGE: return "vector length D must be at least 1";
-    case CS_ERR_SCALE: return "scale must be finite and nonzero";
+    case CS_ERR_SCALE:
+      return "scale must be finite and nonzero, and scale / temperature within the fp32 range";
     case CS_ERR_TEMPERATURE: return "temperature must be finite and positive";
     case CS_ERR_BATCH: return "batch size B must be at least 1";
     case CS_ERR_SIMILARITY: return "similarity must be CS_SIM_DOT or CS_SIM_COSINE";

@@ -72,7 +72,8 @@ extern "C" {
 #define CS_ERR_NULL_POINTER (-1) /* query (page), candidates or out (reading) is NULL */
 #define CS_ERR_K_RANGE (-2)      /* K < 1 or K > 255 (page) */
 #define CS_ERR_D_RANGE (-3)      /* D < 1 (page) */
-#define CS_ERR_SCALE (-4)        /* scale == 0 (page), NaN or infinite (reading) */
+#define CS_ERR_SCALE (-4)        /* scale == 0 (page), NaN or infinite, or scale /
+                                    temperature beyond the fp32 range (reading) */
 #define CS_ERR_TEMPERATURE (-5)  /* temperature < 0 (page), 0, NaN or infinite (reading) */
 #define CS_ERR_BATCH (-6)        /* B < 1 (reading) */
 #define CS_ERR_SIMILARITY (-7)   /* similarity is neither CS_SIM_DOT nor CS_SIM_COSINE */

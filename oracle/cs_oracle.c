@@ -43,6 +43,9 @@ int cso_validate(int query_present, int candidates_present, int out_present,
   /* A negative temperature is rejected; zero, NaN and infinities are too,
    * since z = scale * s / T is undefined or degenerate there (reading). */
   if (!(temperature > 0.0f) || isinf(temperature)) return CSO_ERR_TEMPERATURE;
+  /* The call forms its logits in fp32 (the page's precision) with the factor
+   * scale / T; a factor beyond the fp32 range is rejected (reading). */
+  if (isinf((float)((double)scale / (double)temperature))) return CSO_ERR_SCALE;
   return CSO_OK;
 }
 
