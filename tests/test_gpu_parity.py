@@ -359,3 +359,17 @@ def test_unfused_general_shapes(cs, orc, dev, D, offset):
         assert st == 0
         torch.cuda.synchronize()
         check(out.cpu().numpy(), want, f"unfused D={D} {sim}")
+
+
+@pytest.mark.parametrize("sim", ["dot", "cosine"])
+def test_batch_beyond_the_grid_cap(cs, orc, dev, sim):
+    """More questions than the launch's grid cap (2^20 workgroups): the
+    workgroups stride over the remaining questions. Every element is checked
+    against the oracle."""
+    B, K, D = (1 << 20) + 37, 3, 4
+    st, grid, block, groups = cs.cs_plan_launch(B, K, D, sim, False)
+    assert st == 0 and grid == 1 << 20 and groups == 1, (st, grid, groups)
+    Q, C = workloads.normal_inputs(120 if sim == "dot" else 121, B, K, D)
+    note(f"case grid cap B={B} K={K} D={D} {sim} grid={grid} block={block}")
+    p = run(cs, Q, C, sim, 2.0, 1.0, dev, "batch", groups=1)
+    check(p, orc.score(Q, C, sim, 2.0), f"grid cap {sim}")

@@ -142,3 +142,15 @@ def test_ragged_full_size_sampled(cs, orc):
         err = float(np.max(np.abs(p[lo:hi].astype(np.float64) - want)))
         assert err <= TOL, (b, err)
     note(f"  sampled questions {sample}: ok")
+
+
+def test_ragged_beyond_the_grid_cap(cs, orc):
+    """More questions than the launch's grid cap (2^20 workgroups), in index
+    order (the questions are far too small for the longest-first ranking to
+    pay): the workgroups stride over the rest. Every row is checked."""
+    B, D = (1 << 20) + 11, 4
+    offsets = workloads.ragged_offsets(131, B, k_max=3)
+    Q, C = workloads.ragged_inputs(137, offsets, D)
+    note(f"case ragged grid cap B={B} D={D} rows={offsets[-1]}")
+    p = run_ragged(cs, Q, C, offsets, "cosine", 2.0)
+    check(p, orc.score_ragged(Q, C, offsets, "cosine", 2.0), offsets, "ragged grid cap")
