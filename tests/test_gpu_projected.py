@@ -134,3 +134,15 @@ def test_projected_full_size_sampled(cs, orc, dev, name):
     check(p[sample], want(orc, w, questions=sample), f"{name} sampled")
     sums = np.abs(p.astype(np.float64).sum(axis=1) - 1.0)
     assert float(sums.max()) <= 1e-5
+
+
+@pytest.mark.parametrize("sim", ["dot", "cosine"])
+def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
+    """More questions than the scoring launch's grid cap (2^20 workgroups):
+    the candidate pass (dot) and the register-staged cosine tile (a hidden
+    size below one 64-wide chunk) stride over the rest. Every element is
+    checked against the oracle."""
+    B, K, Hq, Hc, P = (1 << 20) + 5, 2, 8, 8, 64
+    w = workloads.projected_inputs(141 if sim == "dot" else 143, B, K, Hq, Hc, P, sim)
+    note(f"case projected grid cap B={B} K={K} Hq={Hq} Hc={Hc} P={P} {sim}")
+    check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
