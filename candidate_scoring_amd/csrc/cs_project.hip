@@ -180,31 +180,39 @@ __device__ __forceinline__ void pack_wt_block(const uint16_t* __restrict__ w,
 
 // ---------------------------------------------------------------------------
 // q'[b][p] = sum_h x[b][h] * w[p][h]  (x [B][H], w [P][H], bf16; H % 8 == 0)
-// on the matrix cores. One workgroup of 16 waves per 32 x 32 tile of q'; the
-// hidden sum is split over the waves in 64-wide blocks (wave w takes blocks
-// w, w+16, ...), and a wave issues the loads of two blocks before
-// its first multiply, so the tile's operands are in flight at once. Both
-// operands come straight from global memory as v_mfma_f32_16x16x32_bf16
-// fragments (the same hidden indices pair up on both sides, which is all a
-// contraction needs). bf16 products are exact in fp32; the 16 partial tiles
-// are added in wave order through LDS.
-constexpr int kPqWaves = 16;
-constexpr int kPqDepth = 2;  // blocks in flight per wave
+// on the matrix cores (v_mfma_f32_16x16x32_bf16; bf16 products are exact in
+// fp32). One workgroup of 8 waves per 32 x 32 tile of q'; the hidden sum is
+// split over the waves in 32-wide blocks (wave w takes blocks w, w+8, ...),
+// and a wave issues the loads of up to R blocks before its first multiply,
+// so its share of the tile's operands is in flight at once. The 8 partial
+// tiles are added in wave order through LDS.
+//
+// The operands are loaded contiguously, four lanes to a row's 64-byte run
+// of a block (lane l: row l/4 of a 16-row half, 16-byte piece l%4), and
+// each wave passes them through a private LDS slot to reach the fragment
+// layout (lane l: row l%16, piece l/16). Loading fragments straight from
+// global memory puts 16 rows in one instruction with no two neighbouring
+// lanes in the same row, which costs the L1 one lookup per lane instead of
+// one per four and bounded the kernel.
+constexpr int kPqWaves = 8;
 
+__device__ __forceinline__ void mfma_block(f32x4_t (&acc)[2][2], const bf16x8_t (&a)[2],
+                                           const bf16x8_t (&b)[2]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+}
+
+template <int R>
 __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ q,
     uint16_t* __restrict__ parts, int B, int H, int P, const uint16_t* __restrict__ wc,
     uint16_t* __restrict__ wpack, int Hc) {
   __shared__ float part[kPqWaves][16][kWave];
+  __shared__ uint4 stage[kPqWaves][2][4][kWave];  // [wave][slot][x0, x1, w0, w1][lane]
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (wpack != nullptr) {
-    // This workgroup's share of the fold's W^T packing (independent of q').
-    const long long total = pack_wt_blocks(Hc, P);
-    const long long per = (total + gridDim.x - 1) / gridDim.x;
-    const long long end = min(total, per * ((long long)blockIdx.x + 1));
-    for (long long t = per * blockIdx.x + tid; t < end; t += blockDim.x)
-      pack_wt_block(wc, wpack, Hc, P, t);
-  }
   const int ptiles = (P + 31) / 32;
   // Consecutive workgroups go to different XCDs (each with its own L2), so
   // when the grid divides evenly, XCD j is given tiles j*(grid/8) ..: the
@@ -214,19 +222,6 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
   if (gridDim.x % 8 == 0) tile = (long long)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   const long long b0 = (tile / ptiles) * 32;
   const int p0 = (int)(tile % ptiles) * 32;
-  // v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of a 16-row block and
-  // hidden elements 8*(l/16) .. +8 of a 32-wide step, so the four lanes of a
-  // row read 64 contiguous bytes and one 16-byte-per-lane load touches 16
-  // rows (with 32x32x16 fragments it touched 32, each row's cache line looked
-  // up once per 32 bytes). A workgroup's 32 x 32 tile is 2 x 2 such blocks.
-  const int r16 = lane & 15, kq = lane >> 4;
-  const uint16_t* xr[2];
-  const uint16_t* wr[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    xr[h] = x + (size_t)min(b0 + 16 * h + r16, (long long)B - 1) * (size_t)H;
-    wr[h] = w + (size_t)min(p0 + 16 * h + r16, P - 1) * (size_t)H;
-  }
   f32x4_t acc4[2][2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -234,40 +229,73 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc4[rb][cb][i] = 0.0f;
-  const int nblk = (H + 63) / 64;
-  for (int kb0 = wave; kb0 < nblk; kb0 += kPqDepth * kPqWaves) {
-    bf16x8_t av[kPqDepth][2][2], wv[kPqDepth][2][2];  // [block][row half][k-step]
+
+  // Whole 32-wide blocks: wave w takes blocks w + 8 j, j < mine.
+  const int nfull = H / 32;
+  const int mine = (nfull - wave + kPqWaves - 1) / kPqWaves;
+  const int r4 = lane >> 2, pc = lane & 3;
+  const uint16_t* cr[4];  // this lane's rows of x (two 16-row halves), then of w
 #pragma unroll
-    for (int d = 0; d < kPqDepth; ++d) {
-      const int kb = kb0 + d * kPqWaves;
+  for (int h = 0; h < 2; ++h) {
+    cr[h] = x + (size_t)min(b0 + 16 * h + r4, (long long)B - 1) * (size_t)H;
+    cr[2 + h] = w + (size_t)min(p0 + 16 * h + r4, P - 1) * (size_t)H;
+  }
+  // LDS positions: the piece index is XORed with bits 1..2 of the row, so
+  // the eight lanes of an LDS pass (two rows of four pieces when writing,
+  // eight rows of one piece when reading) hit eight distinct 16-byte bank
+  // groups.
+  const int wslot = r4 * 4 + (pc ^ ((r4 >> 1) & 3));
+  const int rrow = lane & 15, rpc = lane >> 4;
+  const int rslot = rrow * 4 + (rpc ^ ((rrow >> 1) & 3));
+  for (int r0 = 0; r0 < mine; r0 += R) {
+    uint4 cv[R][4];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int k = 64 * kb + 32 * st + 8 * kq;
+    for (int i = 0; i < R; ++i) {
+      // Past this wave's blocks the load repeats its last block (always in
+      // bounds); the products of those repeats are zeroed below.
+      const int k = 32 * (wave + kPqWaves * min(r0 + i, mine - 1)) + 8 * pc;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (kb < nblk && k < H) {
-            av[d][h][st] = *reinterpret_cast<const bf16x8_t*>(xr[h] + k);
-            wv[d][h][st] = *reinterpret_cast<const bf16x8_t*>(wr[h] + k);
-          } else {
+      for (int t = 0; t < 4; ++t) cv[i][t] = *reinterpret_cast<const uint4*>(cr[t] + k);
+    }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              av[d][h][st][e] = (__bf16)0.0f;
-              wv[d][h][st][e] = (__bf16)0.0f;
-            }
-          }
+    for (int i = 0; i < R; ++i) {
+      // A select rather than a branch: a branch here would split the round
+      // and let the compiler sink each block's loads down to their use.
+      const bool use = r0 + i < mine;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) stage[wave][i & 1][t][wslot] = cv[i][t];
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 ra = stage[wave][i & 1][h][rslot], rb = stage[wave][i & 1][2 + h][rslot];
+        fa[h] = __builtin_bit_cast(bf16x8_t, use ? ra : z);
+        fb[h] = __builtin_bit_cast(bf16x8_t, use ? rb : z);
+      }
+      mfma_block(acc4, fa, fb);
+    }
+  }
+  if (H % 32 != 0 && wave == nfull % kPqWaves) {
+    // The last, partial block, loaded straight into the fragment layout;
+    // lanes past H contribute zeros.
+    const int k = 32 * nfull + 8 * rpc;
+    bf16x8_t fa[2], fb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t xrow = (size_t)min(b0 + 16 * h + rrow, (long long)B - 1);
+      const size_t wrow = (size_t)min(p0 + 16 * h + rrow, P - 1);
+      if (k < H) {
+        fa[h] = *reinterpret_cast<const bf16x8_t*>(x + xrow * (size_t)H + k);
+        fb[h] = *reinterpret_cast<const bf16x8_t*>(w + wrow * (size_t)H + k);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          fa[h][e] = (__bf16)0.0f;
+          fb[h][e] = (__bf16)0.0f;
         }
       }
     }
-#pragma unroll
-    for (int d = 0; d < kPqDepth; ++d)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d][rb][st], wv[d][cb][st],
-                                                                   acc4[rb][cb], 0, 0, 0);
+    mfma_block(acc4, fa, fb);
   }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -277,24 +305,33 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
       for (int i = 0; i < 4; ++i) part[wave][4 * (2 * rb + cb) + i][lane] = acc4[rb][cb][i];
   __syncthreads();
   // Element i of tile (rb, cb) in lane l is q'[b0 + 16*rb + 4*(l/16) + i][p0 + 16*cb + l%16].
-  {
-    const int e = tid / kWave, l = tid % kWave;  // 1024 threads, 16 x 64 outputs
+  for (int e = wave; e < 16; e += kPqWaves) {
     float v = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][l];
+    for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][lane];
     const int t = e / 4, i = e % 4, rb = t / 2, cb = t % 2;
-    const long long b = b0 + 16 * rb + 4 * (l / 16) + i;
-    const int pp = p0 + 16 * cb + (l & 15);
-    if (b < B && pp < P) q[(size_t)b * (size_t)P + pp] = v;
+    const long long bq = b0 + 16 * rb + 4 * (lane / 16) + i;
+    const int pp = p0 + 16 * cb + (lane & 15);
+    if (bq < B && pp < P) q[(size_t)bq * (size_t)P + pp] = v;
     const int p16 = (P + 15) / 16 * 16;
-    if (parts != nullptr && b < B && pp < p16) {
+    if (parts != nullptr && bq < B && pp < p16) {
       float3 sp = make_float3(0.0f, 0.0f, 0.0f);
       if (pp < P) sp = split3(v);
       const int nks = 3 * p16 / 16;
-      parts[frag_offset(b, pp, nks)] = bf16_bits(sp.x);
-      parts[frag_offset(b, p16 + pp, nks)] = bf16_bits(sp.y);
-      parts[frag_offset(b, 2 * p16 + pp, nks)] = bf16_bits(sp.z);
+      parts[frag_offset(bq, pp, nks)] = bf16_bits(sp.x);
+      parts[frag_offset(bq, p16 + pp, nks)] = bf16_bits(sp.y);
+      parts[frag_offset(bq, 2 * p16 + pp, nks)] = bf16_bits(sp.z);
     }
+  }
+  if (wpack != nullptr) {
+    // This workgroup's share of the fold's W^T packing (independent of q'),
+    // after its own loads so that it does not delay them.
+    const long long total = pack_wt_blocks(Hc, P);
+    const long long per = (total + gridDim.x - 1) / gridDim.x;
+    const long long end = min(total, per * ((long long)blockIdx.x + 1));
+    for (long long t = per * blockIdx.x + (long long)lane * kPqWaves + wave; t < end;
+         t += blockDim.x)
+      pack_wt_block(wc, wpack, Hc, P, t);
   }
 }
 
@@ -1001,9 +1038,20 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   {
     const long long groups = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
     // For dot the same launch also packs Wc^T for the fold.
-    hipLaunchKernelGGL(proj_query_mfma, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream,
-                       p.xq, p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P, p.wc,
-                       p.cosine ? nullptr : p.wpack, p.Hc);
+    // Blocks in flight per wave: every whole block of a wave's share up to
+    // ten (more take further rounds), so short hidden sizes issue no
+    // repeated loads.
+    const int per_wave = (p.Hq / 32 + kPqWaves - 1) / kPqWaves;
+    auto launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream, p.xq,
+                         p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P, p.wc,
+                         p.cosine ? nullptr : p.wpack, p.Hc);
+    };
+    if (per_wave <= 1) launch(proj_query_mfma<1>);
+    else if (per_wave <= 2) launch(proj_query_mfma<2>);
+    else if (per_wave <= 4) launch(proj_query_mfma<4>);
+    else if (per_wave <= 6) launch(proj_query_mfma<6>);
+    else launch(proj_query_mfma<10>);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
