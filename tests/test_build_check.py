@@ -26,3 +26,15 @@ def test_spilling_kernels_are_named_with_their_scratch():
 def test_scratch_line_without_a_kernel_name_is_ignored():
     text = "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 12 [-R]\n" + remarks(("k", 0))
     assert build.spilling_kernels(text) == []
+
+
+def test_c_client_is_built_and_links():
+    """The plain C caller used by the GPU tests is built and its libraries
+    resolve (run without arguments it prints its usage and touches no GPU)."""
+    import subprocess
+    from pathlib import Path
+
+    client = Path(__file__).resolve().parent / "c_client" / "cs_client"
+    assert client.exists(), "run __graft_entry__.build()"
+    r = subprocess.run([str(client)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage: cs_client IN OUT" in r.stderr, r.stderr
