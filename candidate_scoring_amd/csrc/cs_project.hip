@@ -15,7 +15,8 @@
 //    u, with the same in-workgroup softmax as the plain scoring kernels. The
 //    candidate side stays a bandwidth-bound pass; no candidate is projected.
 //  * cosine (CLM): the norm |Wc x_k| needs the projected rows, a dense
-//    contraction: proj_cos_mfma computes, per question, the tile
+//    contraction: proj_cos_mfma_async (hidden sizes in whole 64-wide chunks;
+//    proj_cos_mfma otherwise) computes, per question, the tile
 //    C' = X Wc^T (255 x P, X [K][Hc]) with v_mfma_f32_32x32x16_bf16, keeps it
 //    in registers, and reduces each row to (c'.q', |c'|^2) in its epilogue;
 //    the projected candidates never reach global memory.
