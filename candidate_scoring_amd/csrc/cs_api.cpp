@@ -34,10 +34,17 @@ constexpr int kMaxSplitWaves = 4;  // a slice of a split question: up to 256 thr
 // write-back, which the chip serialises at roughly 20 ns each) plus a merge.
 // With a workgroup streaming about 120 GB/s, the time
 //   bytes_q / (G * 120 GB/s) + B * G * 20 ns
-// is smallest at G* = sqrt(bytes_q / (B * 2400 B)). Splitting pays only when
-// G* is large enough to beat one fuller workgroup per question; measured on
-// MI355X for K = 255, D = 512 and 2560, B = 1 .. 1024, that is G* >= 5.
+// is smallest at G* = sqrt(bytes_q / (B * 2400 B)). Measured on MI355X (K =
+// 255, D from 512 to 4096, B from 1 to 32, every slice count), the fastest
+// counts sit somewhat above G* (fewer rows per slice cut the dependent load
+// rounds of each wave), and splitting pays from G* >= 3.5 on. G = 1.2 G*,
+// with its rows per slice rounded to whole load rounds and at most one
+// slice workgroup per compute unit (plan_groups), is within 8 % of the best
+// measured count at every point and 1.5 % on average; G* itself with a
+// threshold of 5 lost up to 1.8x (B = 32, D = 1536: one workgroup per
+// question left most compute units idle).
 constexpr double kSliceBalanceBytes = 2400.0;
+constexpr double kSliceScale = 1.2;
 // The merge adds about 2 us (release, ticket, acquire, rescale), so a
 // question that one 8-wave workgroup streams in less than that (about
 // 160 GB/s x 2 us = 320 KB) is never split.
@@ -51,8 +58,10 @@ constexpr double kRankCostRatio = 32.0;
 // Candidate blocks larger than all eight XCD L2 caches together are streamed
 // with non-temporal loads.
 constexpr double kStreamBytes = 32.0 * 1024 * 1024;
-constexpr double kMinUsefulSlices = 5.0;
+constexpr double kMinUsefulSlices = 3.5;
 constexpr int kMaxSlices = 64;
+// Compute units of MI355X: the most slice workgroups a batch is given.
+constexpr int kMaxSliceWorkgroups = 256;
 // Grid cap; items beyond it are strided over the resident workgroups.
 constexpr long long kGridCap = 1 << 20;
 
@@ -127,8 +136,23 @@ int plan_groups(int B, int K, int D) {
   if (bytes_q < kMinSplitBytes) return 1;
   const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
   if (g_star < kMinUsefulSlices) return 1;
-  const int G = std::min({K, kMaxSlices, (int)std::lround(g_star)});
-  const int rpg = (K + G - 1) / G;
+  int G = std::max(2, std::min({K, kMaxSlices, (int)std::lround(kSliceScale * g_star)}));
+  // Whole load rounds: a slice's rows are loaded by up to kMaxSplitWaves
+  // waves of R rows each (R of the kernel variant D selects), so rows just
+  // past a multiple of that cost a whole further round of latency; the rows
+  // per slice are rounded to the nearest multiple (ties down).
+  const int nv = D % 4 == 0 ? cs::regq_nv_for(D) : 0;
+  const int per_round = kMaxSplitWaves * (nv > 0 ? cs::regq_rows_per_wave(nv) : 4);
+  int rpg = (K + G - 1) / G;
+  if (rpg > per_round) {
+    rpg = std::max(per_round, (rpg + per_round / 2 - 1) / per_round * per_round);
+    G = (K + rpg - 1) / rpg;
+  }
+  // At most one slice workgroup per compute unit: past that, two slices
+  // share a unit and the batch took 30-50 % longer.
+  G = std::min(G, std::max(1, kMaxSliceWorkgroups / B));
+  if (G < 2) return 1;
+  rpg = (K + G - 1) / G;
   return (K + rpg - 1) / rpg;  // no empty slices
 }
 
