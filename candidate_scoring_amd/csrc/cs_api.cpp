@@ -130,19 +130,19 @@ int device_compute_units() {
   return n;
 }
 
-int plan_groups(int B, int K, int D) {
+// Slices per question for a candidate pass that streams bytes_q per question
+// with waves of R rows each (the shared core of both planners).
+int plan_slices(int B, int K, double bytes_q, int R) {
   if (K == 1) return 1;
-  const double bytes_q = 4.0 * (double)K * (double)D;
   if (bytes_q < kMinSplitBytes) return 1;
   const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
   if (g_star < kMinUsefulSlices) return 1;
   int G = std::max(2, std::min({K, kMaxSlices, (int)std::lround(kSliceScale * g_star)}));
   // Whole load rounds: a slice's rows are loaded by up to kMaxSplitWaves
-  // waves of R rows each (R of the kernel variant D selects), so rows just
-  // past a multiple of that cost a whole further round of latency; the rows
-  // per slice are rounded to the nearest multiple (ties down).
-  const int nv = D % 4 == 0 ? cs::regq_nv_for(D) : 0;
-  const int per_round = kMaxSplitWaves * (nv > 0 ? cs::regq_rows_per_wave(nv) : 4);
+  // waves of R rows each, so rows just past a multiple of that cost a whole
+  // further round of latency; the rows per slice are rounded to the nearest
+  // multiple (ties down).
+  const int per_round = kMaxSplitWaves * R;
   int rpg = (K + G - 1) / G;
   if (rpg > per_round) {
     rpg = std::max(per_round, (rpg + per_round / 2 - 1) / per_round * per_round);
@@ -154,6 +154,13 @@ int plan_groups(int B, int K, int D) {
   if (G < 2) return 1;
   rpg = (K + G - 1) / G;
   return (K + rpg - 1) / rpg;  // no empty slices
+}
+
+// fp32 scoring: R of the kernel variant D selects (the general kernel's 4
+// when no register-query variant covers D).
+int plan_groups(int B, int K, int D) {
+  const int nv = D % 4 == 0 ? cs::regq_nv_for(D) : 0;
+  return plan_slices(B, K, 4.0 * (double)K * (double)D, nv > 0 ? cs::regq_rows_per_wave(nv) : 4);
 }
 
 // Launch shape for a validated call: kernel variant from D and alignment,
@@ -322,10 +329,16 @@ size_t projected_wpack_bytes(int Hc, int P) {
   const size_t p16 = (size_t)(P + 15) / 16 * 16, h32 = (size_t)(Hc + 31) / 32 * 32;
   return align_up(sizeof(uint16_t) * h32 * p16, 256);
 }
+// Dot: the candidate pass's merge tickets and slice partials, sized for the
+// most slices any call plans, so the size does not depend on K.
+size_t projected_split_bytes(int B) {
+  return ticket_bytes(B) + align_up(sizeof(float) * 2 * (size_t)B * (size_t)kMaxSlices, 256);
+}
 size_t projected_workspace(int B, int Hc, int P, int sim) {
   size_t bytes = projected_qp_bytes(B, P);
   if (sim == CS_SIM_DOT)
-    bytes += projected_u_bytes(B, Hc) + projected_parts_bytes(B, P) + projected_wpack_bytes(Hc, P);
+    bytes += projected_u_bytes(B, Hc) + projected_parts_bytes(B, P) + projected_wpack_bytes(Hc, P) +
+             projected_split_bytes(B);
   return bytes;
 }
 
@@ -365,6 +378,17 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
                                         projected_u_bytes(B, Hc));
   p.wpack = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(p.parts) +
                                         projected_parts_bytes(B, P));
+  p.tickets = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(p.wpack) +
+                                          projected_wpack_bytes(Hc, P));
+  p.partials = reinterpret_cast<float2*>(reinterpret_cast<char*>(p.tickets) + ticket_bytes(B));
+  // The dot candidate pass streams 2*K*Hc bytes per question; small batches
+  // spread each question over several workgroups as the fp32 path does. The
+  // query projection zeroes the tickets first, so the workspace needs no
+  // preparation by the caller.
+  p.G = sim == CS_SIM_DOT
+            ? plan_slices(B, K, 2.0 * (double)K * (double)Hc,
+                          cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)))
+            : 1;
   p.B = B;
   p.K = K;
   p.Hq = Hq;

@@ -55,6 +55,9 @@ struct ProjArgs {
   float* u;            // workspace [B][Hc]: folded queries (dot only)
   uint16_t* parts;     // workspace: bf16 split of q', fragment-packed (dot only)
   uint16_t* wpack;     // workspace: Wc^T, fragment-packed (dot only)
+  unsigned* tickets;   // workspace [B]: merge tickets of the split candidate pass (dot only)
+  float2* partials;    // workspace [B][G]: (max, sum) per slice (dot only)
+  int G;               // slices per question of the dot candidate pass (1: no split)
   int B, K, Hq, Hc, P;
   float zscale;        // scale / temperature
   int cosine;

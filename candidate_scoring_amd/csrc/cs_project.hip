@@ -210,7 +210,7 @@ template <int R>
 __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ q,
     uint16_t* __restrict__ parts, int B, int H, int P, const uint16_t* __restrict__ wc,
-    uint16_t* __restrict__ wpack, int Hc) {
+    uint16_t* __restrict__ wpack, int Hc, unsigned* __restrict__ tickets, long long ntiles) {
   __shared__ float part[kPqWaves][16][kWave];
   __shared__ uint4 stage[kPqWaves][2][4][kWave];  // [wave][slot][x0, x1, w0, w1][lane]
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -221,108 +221,116 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
   // one L2 instead of every XCD reading all of x.
   long long tile = blockIdx.x;
   if (gridDim.x % 8 == 0) tile = (long long)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const long long b0 = (tile / ptiles) * 32;
-  const int p0 = (int)(tile % ptiles) * 32;
-  f32x4_t acc4[2][2];
+  // With few questions the grid is widened so that the W^T packing spreads
+  // over every compute unit; workgroups past the last tile only pack.
+  if (tile < ntiles) {
+    const long long b0 = (tile / ptiles) * 32;
+    const int p0 = (int)(tile % ptiles) * 32;
+    f32x4_t acc4[2][2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc4[rb][cb][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) acc4[rb][cb][i] = 0.0f;
 
-  // Whole 32-wide blocks: wave w takes blocks w + 8 j, j < mine.
-  const int nfull = H / 32;
-  const int mine = (nfull - wave + kPqWaves - 1) / kPqWaves;
-  const int r4 = lane >> 2, pc = lane & 3;
-  const uint16_t* cr[4];  // this lane's rows of x (two 16-row halves), then of w
+    // Whole 32-wide blocks: wave w takes blocks w + 8 j, j < mine.
+    const int nfull = H / 32;
+    const int mine = (nfull - wave + kPqWaves - 1) / kPqWaves;
+    const int r4 = lane >> 2, pc = lane & 3;
+    const uint16_t* cr[4];  // this lane's rows of x (two 16-row halves), then of w
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    cr[h] = x + (size_t)min(b0 + 16 * h + r4, (long long)B - 1) * (size_t)H;
-    cr[2 + h] = w + (size_t)min(p0 + 16 * h + r4, P - 1) * (size_t)H;
-  }
-  // LDS positions: the piece index is XORed with bits 1..2 of the row, so
-  // the eight lanes of an LDS pass (two rows of four pieces when writing,
-  // eight rows of one piece when reading) hit eight distinct 16-byte bank
-  // groups.
-  const int wslot = r4 * 4 + (pc ^ ((r4 >> 1) & 3));
-  const int rrow = lane & 15, rpc = lane >> 4;
-  const int rslot = rrow * 4 + (rpc ^ ((rrow >> 1) & 3));
-  for (int r0 = 0; r0 < mine; r0 += R) {
-    uint4 cv[R][4];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      // Past this wave's blocks the load repeats its last block (always in
-      // bounds); the products of those repeats are zeroed below.
-      const int k = 32 * (wave + kPqWaves * min(r0 + i, mine - 1)) + 8 * pc;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) cv[i][t] = *reinterpret_cast<const uint4*>(cr[t] + k);
+    for (int h = 0; h < 2; ++h) {
+      cr[h] = x + (size_t)min(b0 + 16 * h + r4, (long long)B - 1) * (size_t)H;
+      cr[2 + h] = w + (size_t)min(p0 + 16 * h + r4, P - 1) * (size_t)H;
     }
+    // LDS positions: the piece index is XORed with bits 1..2 of the row, so
+    // the eight lanes of an LDS pass (two rows of four pieces when writing,
+    // eight rows of one piece when reading) hit eight distinct 16-byte bank
+    // groups.
+    const int wslot = r4 * 4 + (pc ^ ((r4 >> 1) & 3));
+    const int rrow = lane & 15, rpc = lane >> 4;
+    const int rslot = rrow * 4 + (rpc ^ ((rrow >> 1) & 3));
+    for (int r0 = 0; r0 < mine; r0 += R) {
+      uint4 cv[R][4];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      // A select rather than a branch: a branch here would split the round
-      // and let the compiler sink each block's loads down to their use.
-      const bool use = r0 + i < mine;
+      for (int i = 0; i < R; ++i) {
+        // Past this wave's blocks the load repeats its last block (always in
+        // bounds); the products of those repeats are zeroed below.
+        const int k = 32 * (wave + kPqWaves * min(r0 + i, mine - 1)) + 8 * pc;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) stage[wave][i & 1][t][wslot] = cv[i][t];
+        for (int t = 0; t < 4; ++t) cv[i][t] = *reinterpret_cast<const uint4*>(cr[t] + k);
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        // A select rather than a branch: a branch here would split the round
+        // and let the compiler sink each block's loads down to their use.
+        const bool use = r0 + i < mine;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) stage[wave][i & 1][t][wslot] = cv[i][t];
+        bf16x8_t fa[2], fb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+          const uint4 ra = stage[wave][i & 1][h][rslot], rb = stage[wave][i & 1][2 + h][rslot];
+          fa[h] = __builtin_bit_cast(bf16x8_t, use ? ra : z);
+          fb[h] = __builtin_bit_cast(bf16x8_t, use ? rb : z);
+        }
+        mfma_block(acc4, fa, fb);
+      }
+    }
+    if (H % 32 != 0 && wave == nfull % kPqWaves) {
+      // The last, partial block, loaded straight into the fragment layout;
+      // lanes past H contribute zeros.
+      const int k = 32 * nfull + 8 * rpc;
       bf16x8_t fa[2], fb[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        const uint4 ra = stage[wave][i & 1][h][rslot], rb = stage[wave][i & 1][2 + h][rslot];
-        fa[h] = __builtin_bit_cast(bf16x8_t, use ? ra : z);
-        fb[h] = __builtin_bit_cast(bf16x8_t, use ? rb : z);
+        const size_t xrow = (size_t)min(b0 + 16 * h + rrow, (long long)B - 1);
+        const size_t wrow = (size_t)min(p0 + 16 * h + rrow, P - 1);
+        if (k < H) {
+          fa[h] = *reinterpret_cast<const bf16x8_t*>(x + xrow * (size_t)H + k);
+          fb[h] = *reinterpret_cast<const bf16x8_t*>(w + wrow * (size_t)H + k);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            fa[h][e] = (__bf16)0.0f;
+            fb[h][e] = (__bf16)0.0f;
+          }
+        }
       }
       mfma_block(acc4, fa, fb);
     }
-  }
-  if (H % 32 != 0 && wave == nfull % kPqWaves) {
-    // The last, partial block, loaded straight into the fragment layout;
-    // lanes past H contribute zeros.
-    const int k = 32 * nfull + 8 * rpc;
-    bf16x8_t fa[2], fb[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const size_t xrow = (size_t)min(b0 + 16 * h + rrow, (long long)B - 1);
-      const size_t wrow = (size_t)min(p0 + 16 * h + rrow, P - 1);
-      if (k < H) {
-        fa[h] = *reinterpret_cast<const bf16x8_t*>(x + xrow * (size_t)H + k);
-        fb[h] = *reinterpret_cast<const bf16x8_t*>(w + wrow * (size_t)H + k);
-      } else {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          fa[h][e] = (__bf16)0.0f;
-          fb[h][e] = (__bf16)0.0f;
-        }
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][4 * (2 * rb + cb) + i][lane] = acc4[rb][cb][i];
+    __syncthreads();
+    // Element i of tile (rb, cb) in lane l is q'[b0 + 16*rb + 4*(l/16) + i][p0 + 16*cb + l%16].
+    for (int e = wave; e < 16; e += kPqWaves) {
+      float v = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][lane];
+      const int t = e / 4, i = e % 4, rb = t / 2, cb = t % 2;
+      const long long bq = b0 + 16 * rb + 4 * (lane / 16) + i;
+      const int pp = p0 + 16 * cb + (lane & 15);
+      if (bq < B && pp < P) q[(size_t)bq * (size_t)P + pp] = v;
+      const int p16 = (P + 15) / 16 * 16;
+      if (parts != nullptr && bq < B && pp < p16) {
+        float3 sp = make_float3(0.0f, 0.0f, 0.0f);
+        if (pp < P) sp = split3(v);
+        const int nks = 3 * p16 / 16;
+        parts[frag_offset(bq, pp, nks)] = bf16_bits(sp.x);
+        parts[frag_offset(bq, p16 + pp, nks)] = bf16_bits(sp.y);
+        parts[frag_offset(bq, 2 * p16 + pp, nks)] = bf16_bits(sp.z);
       }
     }
-    mfma_block(acc4, fa, fb);
-  }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[wave][4 * (2 * rb + cb) + i][lane] = acc4[rb][cb][i];
-  __syncthreads();
-  // Element i of tile (rb, cb) in lane l is q'[b0 + 16*rb + 4*(l/16) + i][p0 + 16*cb + l%16].
-  for (int e = wave; e < 16; e += kPqWaves) {
-    float v = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < kPqWaves; ++ww) v += part[ww][e][lane];
-    const int t = e / 4, i = e % 4, rb = t / 2, cb = t % 2;
-    const long long bq = b0 + 16 * rb + 4 * (lane / 16) + i;
-    const int pp = p0 + 16 * cb + (lane & 15);
-    if (bq < B && pp < P) q[(size_t)bq * (size_t)P + pp] = v;
-    const int p16 = (P + 15) / 16 * 16;
-    if (parts != nullptr && bq < B && pp < p16) {
-      float3 sp = make_float3(0.0f, 0.0f, 0.0f);
-      if (pp < P) sp = split3(v);
-      const int nks = 3 * p16 / 16;
-      parts[frag_offset(bq, pp, nks)] = bf16_bits(sp.x);
-      parts[frag_offset(bq, p16 + pp, nks)] = bf16_bits(sp.y);
-      parts[frag_offset(bq, 2 * p16 + pp, nks)] = bf16_bits(sp.z);
-    }
+    // The split candidate pass's merge tickets start at zero: the first tile
+    // of each 32-question block clears its questions' tickets (the candidate
+    // pass runs two launches later on the same stream).
+    if (tickets != nullptr && p0 == 0 && tid < 32 && b0 + tid < B) tickets[b0 + tid] = 0u;
   }
   if (wpack != nullptr) {
     // This workgroup's share of the fold's W^T packing (independent of q'),
@@ -411,6 +419,74 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
   }
 }
 
+// The same fold for batches too small to fill the chip: with few question
+// blocks, one wave per tile walks its 16 dependent steps on a handful of
+// compute units. Here four waves share a tile, each taking a quarter of the
+// contraction with all its loads issued at once (clamped to valid steps, so
+// the count of loads in flight is the same on every path), and the partial
+// tiles are added in wave order through LDS.
+constexpr int kFoldSplitWaves = 4;
+constexpr int kFoldSplitSteps = (256 / 16 + kFoldSplitWaves - 1) / kFoldSplitWaves;  // P <= 256
+
+__global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split(
+    const uint16_t* __restrict__ parts, const uint16_t* __restrict__ wp, float* __restrict__ u,
+    int B, int H, int P) {
+  __shared__ f32x16_t red[kFoldSplitWaves][kFoldNb][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int hgroups = (H + 32 * kFoldNb - 1) / (32 * kFoldNb);
+  const long long qb = blockIdx.x / hgroups;
+  const int hg = (int)(blockIdx.x % hgroups);
+  const int sp = (P + 15) / 16;
+  const int s0 = wave * sp / kFoldSplitWaves, s1 = (wave + 1) * sp / kFoldSplitWaves;
+  const int hblocks = (H + 31) / 32;
+  const uint4* ap = reinterpret_cast<const uint4*>(parts) + (size_t)qb * (3 * sp) * kWave + lane;
+  const uint4* bp = reinterpret_cast<const uint4*>(wp) + lane;
+  uint4 a[kFoldSplitSteps][3], w[kFoldSplitSteps][kFoldNb];
+#pragma unroll
+  for (int i = 0; i < kFoldSplitSteps; ++i) {
+    const int ks = min(s0 + i, sp - 1);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a[i][c] = ap[(size_t)(c * sp + ks) * kWave];
+#pragma unroll
+    for (int nb = 0; nb < kFoldNb; ++nb) {
+      const int hb = min(hg * kFoldNb + nb, hblocks - 1);
+      w[i][nb] = bp[((size_t)hb * sp + ks) * kWave];
+    }
+  }
+  f32x16_t acc[kFoldNb];
+#pragma unroll
+  for (int nb = 0; nb < kFoldNb; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[nb][e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kFoldSplitSteps; ++i)
+    if (s0 + i < s1)
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int nb = 0; nb < kFoldNb; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a[i][c]), __builtin_bit_cast(bf16x8_t, w[i][nb]),
+              acc[nb], 0, 0, 0);
+#pragma unroll
+  for (int nb = 0; nb < kFoldNb; ++nb) red[wave][nb][lane] = acc[nb];
+  __syncthreads();
+  // Wave w sums and stores column block w (kFoldNb == kFoldSplitWaves).
+  const int nb = wave;
+  f32x16_t sum = red[0][nb][lane];
+#pragma unroll
+  for (int kk = 1; kk < kFoldSplitWaves; ++kk) sum += red[kk][nb][lane];
+  const int hcol = 32 * (hg * kFoldNb + nb) + (lane & 31);
+  if (hcol < H) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const long long b = qb * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+      if (b < B) u[(size_t)b * (size_t)H + hcol] = sum[e];
+    }
+  }
+}
+static_assert(kFoldNb == kFoldSplitWaves, "one column block per wave in the split fold's sum");
+
 // ---------------------------------------------------------------------------
 // Dot scoring of bf16 candidate rows against the folded fp32 query u: the
 // register-query kernel's structure with 16-byte pieces of 8 bf16. Lane l
@@ -427,8 +503,15 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int pieces = a.D >> 3;
-  for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+  // Items are (question, slice): with G > 1 slices per question, slice g
+  // takes candidates g*rpg .. and the last slice to finish merges, as in the
+  // fp32 kernels.
+  const int G = a.G;
+  const long long items = (long long)a.B * G;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+    const int b = (int)(item / G), g = (int)(item % G);
     const Question qn{(size_t)b * (size_t)a.K, a.K};
+    const int r0 = g * a.rpg, r1 = min(a.K, r0 + a.rpg);
     for (int idx = tid; idx < NV * kWave; idx += blockDim.x) {
       float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
       if (FULL || idx < pieces) {
@@ -441,13 +524,13 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
     }
     __syncthreads();
     const uint16_t* Xb = xc + qn.row * (size_t)a.D;
-    for (int k0 = wave * R; k0 < a.K; k0 += nwaves * R) {
+    for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
       float acc[R];
       const uint16_t* rows[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         acc[r] = 0.0f;
-        rows[r] = Xb + (size_t)min(k0 + r, a.K - 1) * (size_t)a.D;
+        rows[r] = Xb + (size_t)min(k0 + r, r1 - 1) * (size_t)a.D;
       }
       uint4 c[R][NV];
 #pragma unroll
@@ -466,10 +549,11 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
         for (int r = 0; r < R; ++r) acc[r] = dot8_bf(c[r][j], ur, acc[r]);
       }
       const float total = wave_reduce_transposed<R>(acc, lane, OpSum());
-      store_group<false, R>(s, total, lane, k0, 0, a.K);
+      store_group<false, R>(s, total, lane, k0, r0, r1);
     }
     __syncthreads();
-    if (wave == 0) slice_softmax<false>(s, a, qn, b, 0, 0, a.K, a.zscale, lane);
+    if (wave == 0) slice_softmax<false>(s, a, qn, b, g, r0, r1 - r0, a.zscale, lane);
+    if (G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
 }
@@ -975,8 +1059,10 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
   // Four waves per question: at 127 registers a CU holds four such
   // workgroups, so a 1024-question batch is resident at once (eight-wave
   // workgroups ran in two rounds and measured about 1 % slower).
-  const int waves = std::max(1, std::min(4, (p.K + R - 1) / R));
-  const unsigned grid = (unsigned)std::min(p.B, 1 << 20), block = (unsigned)(waves * kWave);
+  const int rpg = (p.K + p.G - 1) / p.G;
+  const int waves = std::max(1, std::min(4, (rpg + R - 1) / R));
+  const unsigned grid = (unsigned)std::min<long long>((long long)p.B * p.G, 1 << 20);
+  const unsigned block = (unsigned)(waves * kWave);
   switch (nv) {
     case 1: return launch_bf16_dot_nv<1, 8, NT>(a, p, grid, block, stream);
     case 2: return launch_bf16_dot_nv<2, 4, NT>(a, p, grid, block, stream);
@@ -1037,7 +1123,11 @@ int bf16_nv_for(int Hc) {
 hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
   {
-    const long long groups = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
+    const long long tiles = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
+    // Dot also packs Wc^T in this launch: at least one workgroup per compute
+    // unit, so that a small batch does not pack it on a few of them.
+    const long long cus = p.compute_units > 0 ? p.compute_units : 256;
+    const long long groups = p.cosine ? tiles : std::max(tiles, cus);
     // For dot the same launch also packs Wc^T for the fold.
     // Blocks in flight per wave: every whole block of a wave's share up to
     // ten (more take further rounds), so short hidden sizes issue no
@@ -1046,7 +1136,8 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
     auto launch = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream, p.xq,
                          p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P, p.wc,
-                         p.cosine ? nullptr : p.wpack, p.Hc);
+                         p.cosine ? nullptr : p.wpack, p.Hc,
+                         p.cosine || p.G <= 1 ? nullptr : p.tickets, tiles);
     };
     if (per_wave <= 1) launch(proj_query_mfma<1>);
     else if (per_wave <= 2) launch(proj_query_mfma<2>);
@@ -1061,18 +1152,26 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.B = p.B;
   a.K = p.K;
   a.D = p.Hc;
-  a.G = 1;
-  a.rpg = p.K;
+  a.G = p.cosine ? 1 : p.G;
+  a.rpg = (p.K + a.G - 1) / a.G;
+  a.tickets = a.G > 1 ? p.tickets : nullptr;
+  a.partials = a.G > 1 ? p.partials : nullptr;
   a.zscale = p.zscale;
   a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
   // u = Wc^T q' (one wave per 32 questions x 128 h), then one
   // bandwidth-bound pass over the candidates.
   {
-    const long long waves =
+    const long long tiles =
         (long long)((p.B + 31) / 32) * ((p.Hc + 32 * kFoldNb - 1) / (32 * kFoldNb));
-    hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
-                       p.parts, p.wpack, p.u, p.B, p.Hc, p.P);
+    const long long cus = p.compute_units > 0 ? p.compute_units : 256;
+    if (tiles < cus)  // too few tiles to fill the chip: four waves per tile
+      hipLaunchKernelGGL(fold_query_mfma_split, dim3((unsigned)tiles),
+                         dim3(kFoldSplitWaves * kWave), 0, stream, p.parts, p.wpack, p.u, p.B,
+                         p.Hc, p.P);
+    else
+      hipLaunchKernelGGL(fold_query_mfma, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream,
+                         p.parts, p.wpack, p.u, p.B, p.Hc, p.P);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -83,6 +83,9 @@ def dev(cs):
     (3, 255, 64, 2048, 64, "dot"),         # four 16-byte pieces per lane
     (2, 50, 520, 1000, 200, "dot"),        # P not a multiple of 16 or 32
     (1, 255, 4096, 4096, 256, "cosine"),   # one question, 64 chunks of the DMA ring
+    (1, 255, 2560, 2560, 256, "dot"),      # one question: the candidate pass is split
+    (2, 200, 512, 1000, 96, "dot"),        # split, a partial last slice
+    (200, 40, 256, 2048, 128, "dot"),      # 7 question blocks: the fold's four-wave tiles
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
@@ -146,3 +149,27 @@ def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
     w = workloads.projected_inputs(141 if sim == "dot" else 143, B, K, Hq, Hc, P, sim)
     note(f"case projected grid cap B={B} K={K} Hq={Hq} Hc={Hc} P={P} {sim}")
     check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
+
+
+def test_projected_split_on_an_unprepared_workspace(cs, orc, dev):
+    """A small dot batch spreads each question's candidate pass over several
+    workgroups, merged through tickets in the workspace; the query projection
+    clears them, so a workspace full of garbage (and then the one a previous
+    call left) gives the same correct result."""
+    import torch
+
+    w = workloads.projected_inputs(151, 3, 255, 2560, 2560, 256, "dot")
+    assert cs.cs_plan_groups(3, 255, 1280, "dot", True) > 1  # the same bytes per question
+    xq, xc = to_dev16(w.xq_bits, dev), to_dev16(w.xc_bits, dev)
+    wq, wc = to_dev16(w.wq_bits, dev), to_dev16(w.wc_bits, dev)
+    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, "dot")
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
+    ref = want(orc, w)
+    note("case projected split, workspace of 0xFF bytes, two calls")
+    for call in range(2):
+        out = torch.full((w.B, w.K), -3.0, device=dev)
+        st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, "dot",
+                                   float(w.scale), 1.0, out, ws, nbytes)
+        assert st == 0, st
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), ref, f"unprepared workspace, call {call}")
