@@ -37,12 +37,13 @@ constexpr int kMaxSplitWaves = 4;  // a slice of a split question: up to 256 thr
 // is smallest at G* = sqrt(bytes_q / (B * 2400 B)). Measured on MI355X (K =
 // 255, D from 512 to 4096, B from 1 to 32, every slice count), the fastest
 // counts sit somewhat above G* (fewer rows per slice cut the dependent load
-// rounds of each wave), and splitting pays from G* >= 3.5 on. G = 1.2 G*,
-// with its rows per slice rounded to whole load rounds and at most one
-// slice workgroup per compute unit (plan_groups), is within 8 % of the best
-// measured count at every point and 1.5 % on average; G* itself with a
-// threshold of 5 lost up to 1.8x (B = 32, D = 1536: one workgroup per
-// question left most compute units idle).
+// rounds of each wave), and splitting pays from G* >= 3.5 on (2.5 for
+// questions of 1 MB and more). G = 1.2 G*, with its rows per slice rounded
+// to whole load rounds and at most one slice workgroup per compute unit
+// (plan_slices), is within 9 % of the best measured count at every point
+// (B from 1 to 256) and 1.2 % on average; G* itself with a threshold of 5
+// lost up to 1.8x (B = 32, D = 1536: one workgroup per question left most
+// compute units idle).
 constexpr double kSliceBalanceBytes = 2400.0;
 constexpr double kSliceScale = 1.2;
 // The merge adds about 2 us (release, ticket, acquire, rescale), so a
@@ -59,6 +60,8 @@ constexpr double kRankCostRatio = 32.0;
 // with non-temporal loads.
 constexpr double kStreamBytes = 32.0 * 1024 * 1024;
 constexpr double kMinUsefulSlices = 3.5;
+constexpr double kLargeQuestionBytes = 1.0e6;
+constexpr double kMinUsefulSlicesLarge = 2.5;
 constexpr int kMaxSlices = 64;
 // Compute units of MI355X: the most slice workgroups a batch is given.
 constexpr int kMaxSliceWorkgroups = 256;
@@ -136,7 +139,10 @@ int plan_slices(int B, int K, double bytes_q, int R) {
   if (K == 1) return 1;
   if (bytes_q < kMinSplitBytes) return 1;
   const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
-  if (g_star < kMinUsefulSlices) return 1;
+  // Large questions pay for splitting earlier: one workgroup per question
+  // would leave most compute units idle for a long time.
+  const bool large = bytes_q >= kLargeQuestionBytes;
+  if (g_star < (large ? kMinUsefulSlicesLarge : kMinUsefulSlices)) return 1;
   int G = std::max(2, std::min({K, kMaxSlices, (int)std::lround(kSliceScale * g_star)}));
   // Whole load rounds: a slice's rows are loaded by up to kMaxSplitWaves
   // waves of R rows each, so rows just past a multiple of that cost a whole
