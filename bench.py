@@ -340,6 +340,34 @@ def projected_section(devc, iters=20):
             tf = flops / us / 1e6
             row.update({"flops": flops, "TFLOPs": round(tf, 1),
                         "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        del xq, xc, wq, wc, out, ws
+        # One question of the same heads: latency of the call (small batches
+        # spread the dot path's candidate pass over the chip).
+        w1 = workloads.make_projected(name, B=1)
+        xq, xc, wq, wc = (dev16(w1.xq_bits), dev16(w1.xc_bits), dev16(w1.wq_bits),
+                          dev16(w1.wc_bits))
+        out = torch.empty(1, w1.K, dtype=torch.float32, device=devc.dev)
+        nbytes = cs.cs_projected_workspace_bytes(1, w1.Hc, w1.P, w1.similarity)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=devc.dev)
+
+        def one():
+            st = cs.cs_score_projected(xq, xc, wq, wc, 1, w1.K, w1.Hq, w1.Hc, w1.P,
+                                       w1.similarity, float(w1.scale), 1.0, out, ws, nbytes,
+                                       devc.stream)
+            assert st == 0, st
+
+        for _ in range(20):
+            one()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(devc.stream)
+            for _ in range(200):
+                one()
+            e1.record(devc.stream)
+            torch.cuda.synchronize()
+            best = min(best, 1e3 * e0.elapsed_time(e1) / 200)
+        row["one_question_us_per_call"] = round(best, 2)
         res[name] = row
         log(f"projected {name}: {row}")
         del xq, xc, wq, wc, out, ws
