@@ -296,7 +296,7 @@ def ragged_section(devc, iters=20):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def projected_section(devc, iters=20):
+def projected_section(devc, iters=20, one_question=True):
     """Projection + scoring on the two 1024-question head workloads (bf16
     hidden states and heads): Kev (dot, heads 2560 -> 256, folded into the
     query) and CLM (cosine, heads 512 -> 256, candidate projection on the
@@ -341,6 +341,10 @@ def projected_section(devc, iters=20):
             row.update({"flops": flops, "TFLOPs": round(tf, 1),
                         "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
         del xq, xc, wq, wc, out, ws
+        if not one_question:
+            res[name] = row
+            log(f"projected {name}: {row}")
+            continue
         # One question of the same heads: latency of the call (small batches
         # spread the dot path's candidate pass over the chip).
         w1 = workloads.make_projected(name, B=1)
@@ -536,7 +540,7 @@ def main():
     if not args.no_ragged:
         result["ragged"] = ragged_section(devc)
     if not args.no_projected:
-        result["projected"] = projected_section(devc)
+        result["projected"] = projected_section(devc, one_question=not args.no_latency)
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)
