@@ -81,7 +81,8 @@ def _bits(b, dev):
     return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev)
 
 
-@pytest.mark.parametrize("kind", ["ragged", "projected_dot", "projected_cosine"])
+@pytest.mark.parametrize("kind", ["ragged", "projected_dot", "projected_cosine",
+                                  "projected_dot_split"])
 def test_capture_multi_kernel_paths_replay_exact(cs, kind):
     """The ragged and projection entry points captured into a graph (through
     torch's capture of the current stream) replay to exactly the direct
@@ -105,8 +106,13 @@ def test_capture_multi_kernel_paths_replay_exact(cs, kind):
 
         shape = (rows,)
     else:
-        sim = "dot" if kind == "projected_dot" else "cosine"
-        w = workloads.projected_inputs(73, 300, 40, 136, 256, 128, sim)
+        sim = "cosine" if kind == "projected_cosine" else "dot"
+        if kind == "projected_dot_split":
+            # Two questions of 1.3 MB: the candidate pass is split, merged
+            # through tickets the query projection clears in the same graph.
+            w = workloads.projected_inputs(74, 2, 255, 2560, 2560, 256, sim)
+        else:
+            w = workloads.projected_inputs(73, 300, 40, 136, 256, 128, sim)
         xq, xc = _bits(w.xq_bits, dev), _bits(w.xc_bits, dev)
         wq, wc = _bits(w.wq_bits, dev), _bits(w.wc_bits, dev)
         nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, sim)
