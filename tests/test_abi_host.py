@@ -132,6 +132,21 @@ def test_workspace_and_group_rejections(lib):
     assert lib.cs_workspace_init(None, 64, None) == cs.CS_ERR_NULL_POINTER
 
 
+def test_planned_slices_fit_one_per_compute_unit(lib):
+    """The planner never gives a batch more slice workgroups than MI355X has
+    compute units (past that two slices share a unit), splits large
+    questions in small batches, and keeps a big batch at one workgroup per
+    question."""
+    for D in (512, 1024, 2560, 4096):
+        for B in (1, 2, 3, 8, 31, 48, 96, 128, 129, 256, 1024):
+            G = cs.cs_plan_groups(B, 255, D, 0, True)
+            assert G >= 1 and (G == 1 or B * G <= 256), (B, D, G)
+            if B > 128:
+                assert G == 1, (B, D, G)
+    assert cs.cs_plan_groups(1, 255, 2560, 0, True) >= 32
+    assert cs.cs_plan_groups(48, 255, 1024, 0, True) > 1   # 1 MB questions split early
+
+
 def test_planning_is_pure_and_shared(lib):
     # no workspace: one workgroup per question
     for B, K, D in ((1, 5, 512), (1, 255, 512), (8, 255, 512), (1024, 255, 2560)):
