@@ -431,7 +431,9 @@ constexpr int kFoldSplitSteps = (256 / 16 + kFoldSplitWaves - 1) / kFoldSplitWav
 __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split(
     const uint16_t* __restrict__ parts, const uint16_t* __restrict__ wp, float* __restrict__ u,
     int B, int H, int P) {
-  __shared__ f32x16_t red[kFoldSplitWaves][kFoldNb][kWave];
+  // Partial tiles as four float4 rows per block, lane-contiguous, so each
+  // 16-byte LDS access of a wave covers consecutive banks.
+  __shared__ float4 red[kFoldSplitWaves][kFoldNb][4][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int hgroups = (H + 32 * kFoldNb - 1) / (32 * kFoldNb);
   const long long qb = blockIdx.x / hgroups;
@@ -469,13 +471,31 @@ __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split
               __builtin_bit_cast(bf16x8_t, a[i][c]), __builtin_bit_cast(bf16x8_t, w[i][nb]),
               acc[nb], 0, 0, 0);
 #pragma unroll
-  for (int nb = 0; nb < kFoldNb; ++nb) red[wave][nb][lane] = acc[nb];
+  for (int nb = 0; nb < kFoldNb; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      red[wave][nb][j][lane] =
+          make_float4(acc[nb][4 * j], acc[nb][4 * j + 1], acc[nb][4 * j + 2], acc[nb][4 * j + 3]);
   __syncthreads();
   // Wave w sums and stores column block w (kFoldNb == kFoldSplitWaves).
   const int nb = wave;
-  f32x16_t sum = red[0][nb][lane];
+  f32x16_t sum;
 #pragma unroll
-  for (int kk = 1; kk < kFoldSplitWaves; ++kk) sum += red[kk][nb][lane];
+  for (int j = 0; j < 4; ++j) {
+    float4 t = red[0][nb][j][lane];
+#pragma unroll
+    for (int kk = 1; kk < kFoldSplitWaves; ++kk) {
+      const float4 v = red[kk][nb][j][lane];
+      t.x += v.x;
+      t.y += v.y;
+      t.z += v.z;
+      t.w += v.w;
+    }
+    sum[4 * j] = t.x;
+    sum[4 * j + 1] = t.y;
+    sum[4 * j + 2] = t.z;
+    sum[4 * j + 3] = t.w;
+  }
   const int hcol = 32 * (hg * kFoldNb + nb) + (lane & 31);
   if (hcol < H) {
 #pragma unroll
