@@ -14,6 +14,8 @@
 //    u = Wc^T q' [B][Hc], and fused_bf16_dot streams the bf16 candidate rows once against
 //    u, with the same in-workgroup softmax as the plain scoring kernels. The
 //    candidate side stays a bandwidth-bound pass; no candidate is projected.
+//    For four questions or fewer, proj_query_gemv and fold_query_gemv make
+//    q' and u as matrix-vector products from the heads' own layout instead.
 //  * cosine (CLM): the norm |Wc x_k| needs the projected rows, a dense
 //    contraction: proj_cos_mfma_async (hidden sizes in whole 64-wide chunks;
 //    proj_cos_mfma otherwise) computes, per question, the tile
@@ -506,6 +508,150 @@ __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split
   }
 }
 static_assert(kFoldNb == kFoldSplitWaves, "one column block per wave in the split fold's sum");
+
+// ---------------------------------------------------------------------------
+// The dot path's query side for a batch of at most kGemvMaxB questions. There
+// the 32-question matrix-core tiles would be mostly padding, and packing Wc^T
+// for them costs more than the products, so both heads are applied as plain
+// matrix-vector products straight from their row-major layout, each reading
+// its head once with fp32 accumulation (the bf16 x bf16 products are exact).
+
+constexpr int kGemvMaxB = 4;
+constexpr int kGemvUnroll = 4;  // 512-wide chunks of a head row in flight per wave
+
+// 8 bf16 times 8 bf16, widened exactly and accumulated in order.
+__device__ __forceinline__ float dot8_bf_bf(uint4 w, uint4 x) {
+  float acc = bf_lo(w.x) * bf_lo(x.x);
+  acc = fmaf(bf_hi(w.x), bf_hi(x.x), acc);
+  acc = fmaf(bf_lo(w.y), bf_lo(x.y), acc);
+  acc = fmaf(bf_hi(w.y), bf_hi(x.y), acc);
+  acc = fmaf(bf_lo(w.z), bf_lo(x.z), acc);
+  acc = fmaf(bf_hi(w.z), bf_hi(x.z), acc);
+  acc = fmaf(bf_lo(w.w), bf_lo(x.w), acc);
+  acc = fmaf(bf_hi(w.w), bf_hi(x.w), acc);
+  return acc;
+}
+
+// q'[b][p] = sum_h Wq[p][h] x_q[b][h]: one wave per head row p, its 16-byte
+// pieces spread over the lanes (kGemvUnroll per lane in flight), the
+// questions' matching pieces loaded beside them; per-lane sums are added
+// over the wave. Loads past the row are clamped to its last piece, which is
+// then zeroed, so every lane issues the same loads.
+// Workgroup 0 also clears the merge tickets of the candidate pass.
+template <int NB>
+__global__ __launch_bounds__(256) void proj_query_gemv(const uint16_t* __restrict__ xq,
+                                                       const uint16_t* __restrict__ wq,
+                                                       float* __restrict__ qp, int B, int Hq,
+                                                       int P, unsigned* __restrict__ tickets) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int p = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (tickets != nullptr && blockIdx.x == 0 && (int)threadIdx.x < B) tickets[threadIdx.x] = 0u;
+  if (p >= P) return;  // uniform across the wave
+  const int n = Hq / 8;  // 16-byte pieces per row
+  const uint4* wr = reinterpret_cast<const uint4*>(wq + (size_t)p * (size_t)Hq);
+  const uint4* xr[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    xr[b] = reinterpret_cast<const uint4*>(xq + (size_t)min(b, B - 1) * (size_t)Hq);
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kWave * kGemvUnroll) {  // uniform trip count
+    uint4 w[kGemvUnroll], x[kGemvUnroll][NB];
+#pragma unroll
+    for (int i = 0; i < kGemvUnroll; ++i) {
+      const int c = min(c0 + kWave * i + lane, n - 1);
+      w[i] = wr[c];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) x[i][b] = xr[b][c];
+    }
+#pragma unroll
+    for (int i = 0; i < kGemvUnroll; ++i) {
+      // A clamped piece is zeroed (a bit select, not a branch) so it adds 0.
+      const uint32_t keep = c0 + kWave * i + lane < n ? ~0u : 0u;
+      const uint4 wi = make_uint4(w[i].x & keep, w[i].y & keep, w[i].z & keep, w[i].w & keep);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] += dot8_bf_bf(wi, x[i][b]);
+    }
+  }
+  // Lane l ends with the sum of question l / (64 / NB).
+  const float total = wave_reduce_transposed<NB>(acc, lane, OpSum());
+  const int b = lane / (kWave / NB);
+  if (lane % (kWave / NB) == 0 && b < B) qp[(size_t)b * (size_t)P + p] = total;
+}
+
+// u[b][h] = sum_p q'[b][p] Wc[p][h]: a workgroup takes kFoldGemvCols columns
+// (eight 16-byte pieces of every row) and all P <= 256 rows as 32 row phases;
+// the lane of phase r loads rows r, r + 32, ... in one round, multiplies them
+// by q' staged in LDS, and the phases are then added in order through LDS
+// (padded so that neither the stores nor the column sums collide on a bank).
+constexpr int kFoldGemvCols = 64;
+constexpr int kFoldGemvPieces = kFoldGemvCols / 8;
+constexpr int kFoldGemvPhases = 256 / kFoldGemvPieces;
+constexpr int kFoldGemvRows = 256 / kFoldGemvPhases;  // rows per lane at P = 256
+constexpr int kFoldGemvPad = kFoldGemvPhases + 1;
+
+template <int NB>
+__global__ __launch_bounds__(256) void fold_query_gemv(const float* __restrict__ qp,
+                                                       const uint16_t* __restrict__ wc,
+                                                       float* __restrict__ u, int B, int Hc,
+                                                       int P) {
+  __shared__ float qs[NB][256];
+  __shared__ float red[NB][8][kFoldGemvPad][kFoldGemvPieces];
+  const int tid = threadIdx.x;
+  const int pc = tid % kFoldGemvPieces, ph = tid / kFoldGemvPieces;
+  const int n = Hc / 8;
+  const int piece = min((int)blockIdx.x * kFoldGemvPieces + pc, n - 1);
+  uint4 w[kFoldGemvRows];
+#pragma unroll
+  for (int r = 0; r < kFoldGemvRows; ++r) {
+    const int row = min(ph + kFoldGemvPhases * r, P - 1);
+    w[r] = reinterpret_cast<const uint4*>(wc + (size_t)row * (size_t)Hc)[piece];
+  }
+  // q' of every question and row, zero past P (rows clamped above then add 0).
+#pragma unroll
+  for (int i = tid; i < NB * 256; i += 256) {
+    const int b = i / 256, row = i % 256;
+    const float v = qp[(size_t)min(b, B - 1) * (size_t)P + min(row, P - 1)];
+    qs[b][row] = (b < B && row < P) ? v : 0.0f;
+  }
+  __syncthreads();
+  float acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[b][j] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kFoldGemvRows; ++r) {
+    const int row = ph + kFoldGemvPhases * r;
+    const uint32_t keep = row < P ? ~0u : 0u;  // clamped rows add 0
+    const uint4 x = make_uint4(w[r].x & keep, w[r].y & keep, w[r].z & keep, w[r].w & keep);
+    const float f[8] = {bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y),
+                        bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w)};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float q = qs[b][row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[b][j] = fmaf(q, f[j], acc[b][j]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[b][j][ph][pc] = acc[b][j];
+  __syncthreads();
+  // Thread t sums column 8 * (t % 8) + (t / 8) % 8 of question t / 64.
+  const int b = tid / 64, j = (tid / kFoldGemvPieces) % 8, c = tid % kFoldGemvPieces;
+  if (b < NB) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kFoldGemvPhases; ++r) sum += red[b][j][r][c];
+    const int h = ((int)blockIdx.x * kFoldGemvPieces + c) * 8 + j;
+    if (b < B && h < Hc) u[(size_t)b * (size_t)Hc + h] = sum;
+  }
+}
+static_assert(kFoldGemvPieces * kFoldGemvPhases == 256 && kFoldGemvPhases * kFoldGemvRows == 256,
+              "the small-batch fold covers 256 rows with 256 threads");
 
 // ---------------------------------------------------------------------------
 // Dot scoring of bf16 candidate rows against the folded fp32 query u: the
@@ -1141,6 +1287,36 @@ int bf16_nv_for(int Hc) {
 }
 
 hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
+  KernelArgs a{};
+  a.out = p.out;
+  a.B = p.B;
+  a.K = p.K;
+  a.D = p.Hc;
+  a.G = p.cosine ? 1 : p.G;
+  a.rpg = (p.K + a.G - 1) / a.G;
+  a.tickets = a.G > 1 ? p.tickets : nullptr;
+  a.partials = a.G > 1 ? p.partials : nullptr;
+  a.zscale = p.zscale;
+  a.cosine = p.cosine;
+  if (!p.cosine && p.B <= kGemvMaxB) {
+    // A handful of questions: q' and u as matrix-vector products from the
+    // heads' own layout (no packing); the candidate pass is unchanged.
+    const unsigned qgroups = (unsigned)((p.P + 3) / 4);
+    const unsigned fgroups = (unsigned)((p.Hc / 8 + kFoldGemvPieces - 1) / kFoldGemvPieces);
+    auto launch = [&](auto query, auto fold) {
+      hipLaunchKernelGGL(query, dim3(qgroups), dim3(256), 0, stream, p.xq, p.wq, p.qp, p.B, p.Hq,
+                         p.P, a.tickets);
+      hipLaunchKernelGGL(fold, dim3(fgroups), dim3(256), 0, stream, p.qp, p.wc, p.u, p.B, p.Hc,
+                         p.P);
+    };
+    if (p.B == 1) launch(proj_query_gemv<1>, fold_query_gemv<1>);
+    else if (p.B == 2) launch(proj_query_gemv<2>, fold_query_gemv<2>);
+    else launch(proj_query_gemv<4>, fold_query_gemv<4>);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nv = bf16_nv_for(p.Hc);
+    return p.nt ? launch_bf16_dot<true>(a, p, nv, stream) : launch_bf16_dot<false>(a, p, nv, stream);
+  }
   // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
   {
     const long long tiles = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
@@ -1167,17 +1343,6 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  KernelArgs a{};
-  a.out = p.out;
-  a.B = p.B;
-  a.K = p.K;
-  a.D = p.Hc;
-  a.G = p.cosine ? 1 : p.G;
-  a.rpg = (p.K + a.G - 1) / a.G;
-  a.tickets = a.G > 1 ? p.tickets : nullptr;
-  a.partials = a.G > 1 ? p.partials : nullptr;
-  a.zscale = p.zscale;
-  a.cosine = p.cosine;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
   // u = Wc^T q' (one wave per 32 questions x 128 h), then one
   // bandwidth-bound pass over the candidates.

@@ -86,6 +86,10 @@ def dev(cs):
     (1, 255, 2560, 2560, 256, "dot"),      # one question: the candidate pass is split
     (2, 200, 512, 1000, 96, "dot"),        # split, a partial last slice
     (200, 40, 256, 2048, 128, "dot"),      # 7 question blocks: the fold's four-wave tiles
+    (5, 100, 520, 1000, 96, "dot"),        # one question past the matrix-vector query side
+    (4, 60, 1032, 72, 256, "dot"),         # matrix-vector query side: a partial head row
+                                           # chunk, a partial column strip of the fold
+    (3, 33, 4104, 136, 250, "dot"),        # three chunks per head row, P < 256 clamped rows
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
@@ -151,21 +155,22 @@ def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
     check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
 
 
-def test_projected_split_on_an_unprepared_workspace(cs, orc, dev):
+@pytest.mark.parametrize("B", [3, 6])  # matrix-vector / matrix-core query side
+def test_projected_split_on_an_unprepared_workspace(cs, orc, dev, B):
     """A small dot batch spreads each question's candidate pass over several
     workgroups, merged through tickets in the workspace; the query projection
     clears them, so a workspace full of garbage (and then the one a previous
     call left) gives the same correct result."""
     import torch
 
-    w = workloads.projected_inputs(151, 3, 255, 2560, 2560, 256, "dot")
-    assert cs.cs_plan_groups(3, 255, 1280, "dot", True) > 1  # the same bytes per question
+    w = workloads.projected_inputs(151 + B, B, 255, 2560, 2560, 256, "dot")
+    assert cs.cs_plan_groups(B, 255, 1280, "dot", True) > 1  # the same bytes per question
     xq, xc = to_dev16(w.xq_bits, dev), to_dev16(w.xc_bits, dev)
     wq, wc = to_dev16(w.wq_bits, dev), to_dev16(w.wc_bits, dev)
     nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, "dot")
     ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
     ref = want(orc, w)
-    note("case projected split, workspace of 0xFF bytes, two calls")
+    note(f"case projected split B={B}, workspace of 0xFF bytes, two calls")
     for call in range(2):
         out = torch.full((w.B, w.K), -3.0, device=dev)
         st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, "dot",
