@@ -317,10 +317,10 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   return CS_OK;
 }
 
-// Projected-query workspace: q' [B][P] fp32; for dot also u [B][Hc] fp32,
-// the three-part bf16 split of q' ([B rounded up to 32][3 * P16], P16 = P
-// rounded up to 16) and Wc^T ([Hc rounded up to 32][P16]), both bf16 in
-// matrix-core fragment order.
+// Projected-query workspace: q' [B][P] fp32 and the candidate pass's merge
+// state; for dot also u [B][Hc] fp32, the three-part bf16 split of q'
+// ([B rounded up to 32][3 * P16], P16 = P rounded up to 16) and Wc^T
+// ([Hc rounded up to 32][P16]), both bf16 in matrix-core fragment order.
 size_t projected_qp_bytes(int B, int P) {
   return align_up(sizeof(float) * (size_t)B * (size_t)P, 256);
 }
@@ -335,16 +335,15 @@ size_t projected_wpack_bytes(int Hc, int P) {
   const size_t p16 = (size_t)(P + 15) / 16 * 16, h32 = (size_t)(Hc + 31) / 32 * 32;
   return align_up(sizeof(uint16_t) * h32 * p16, 256);
 }
-// Dot: the candidate pass's merge tickets and slice partials, sized for the
-// most slices any call plans, so the size does not depend on K.
+// The candidate pass's merge tickets and slice partials, sized for the most
+// slices any call plans, so the size does not depend on K.
 size_t projected_split_bytes(int B) {
   return ticket_bytes(B) + align_up(sizeof(float) * 2 * (size_t)B * (size_t)kMaxSlices, 256);
 }
 size_t projected_workspace(int B, int Hc, int P, int sim) {
-  size_t bytes = projected_qp_bytes(B, P);
+  size_t bytes = projected_qp_bytes(B, P) + projected_split_bytes(B);
   if (sim == CS_SIM_DOT)
-    bytes += projected_u_bytes(B, Hc) + projected_parts_bytes(B, P) + projected_wpack_bytes(Hc, P) +
-             projected_split_bytes(B);
+    bytes += projected_u_bytes(B, Hc) + projected_parts_bytes(B, P) + projected_wpack_bytes(Hc, P);
   return bytes;
 }
 
@@ -378,23 +377,32 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.wq = wq;
   p.wc = wc;
   p.out = out;
-  p.qp = static_cast<float*>(ws);
-  p.u = reinterpret_cast<float*>(static_cast<char*>(ws) + projected_qp_bytes(B, P));
-  p.parts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + projected_qp_bytes(B, P) +
-                                        projected_u_bytes(B, Hc));
+  char* const base = static_cast<char*>(ws);
+  p.qp = reinterpret_cast<float*>(base);
+  p.tickets = reinterpret_cast<unsigned*>(base + projected_qp_bytes(B, P));
+  p.partials = reinterpret_cast<float2*>(reinterpret_cast<char*>(p.tickets) + ticket_bytes(B));
+  p.u = reinterpret_cast<float*>(reinterpret_cast<char*>(p.tickets) + projected_split_bytes(B));
+  p.parts = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(p.u) + projected_u_bytes(B, Hc));
   p.wpack = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(p.parts) +
                                         projected_parts_bytes(B, P));
-  p.tickets = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(p.wpack) +
-                                          projected_wpack_bytes(Hc, P));
-  p.partials = reinterpret_cast<float2*>(reinterpret_cast<char*>(p.tickets) + ticket_bytes(B));
-  // The dot candidate pass streams 2*K*Hc bytes per question; small batches
-  // spread each question over several workgroups as the fp32 path does. The
-  // query projection zeroes the tickets first, so the workspace needs no
-  // preparation by the caller.
-  p.G = sim == CS_SIM_DOT
-            ? plan_slices(B, K, 2.0 * (double)K * (double)Hc,
-                          cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)))
-            : 1;
+  // Small batches spread each question's candidate pass over several
+  // workgroups. Dot streams 2*K*Hc bytes per question and is planned like
+  // the fp32 path. Cosine takes one workgroup per 32 candidates when the
+  // batch is small: up to one workgroup per compute unit while no question
+  // is split (K <= 32), up to a quarter of them when questions are split,
+  // since each merge costs a few microseconds of ticket round trips and
+  // the tile kernel (one workgroup per question, the next question's loads
+  // in flight) wins beyond that. The query projection zeroes the tickets
+  // first, so the workspace needs no preparation by the caller.
+  const int ncu = device_compute_units();
+  const int cus = ncu > 0 ? ncu : 256;
+  const int cos_slices = (K + cs::kCosSliceRows - 1) / cs::kCosSliceRows;
+  const long long slice_groups = (long long)B * cos_slices;
+  p.cos_slice =
+      sim == CS_SIM_COSINE && slice_groups <= (cos_slices == 1 ? cus : cus / 4) ? 1 : 0;
+  p.G = sim == CS_SIM_DOT ? plan_slices(B, K, 2.0 * (double)K * (double)Hc,
+                                        cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)))
+                          : (p.cos_slice ? cos_slices : 1);
   p.B = B;
   p.K = K;
   p.Hq = Hq;

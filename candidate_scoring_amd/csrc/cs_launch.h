@@ -55,15 +55,18 @@ struct ProjArgs {
   float* u;            // workspace [B][Hc]: folded queries (dot only)
   uint16_t* parts;     // workspace: bf16 split of q', fragment-packed (dot only)
   uint16_t* wpack;     // workspace: Wc^T, fragment-packed (dot only)
-  unsigned* tickets;   // workspace [B]: merge tickets of the split candidate pass (dot only)
-  float2* partials;    // workspace [B][G]: (max, sum) per slice (dot only)
-  int G;               // slices per question of the dot candidate pass (1: no split)
+  unsigned* tickets;   // workspace [B]: merge tickets of the split candidate pass
+  float2* partials;    // workspace [B][G]: (max, sum) per slice
+  int G;               // slices per question of the candidate pass (1: no split)
+  int cos_slice;       // cosine: one workgroup per kCosSliceRows candidates of a question
   int B, K, Hq, Hc, P;
   float zscale;        // scale / temperature
   int cosine;
   int nt;              // stream the candidate rows non-temporally
   int compute_units;   // compute units of the current device (persistent grids)
 };
+// Candidate rows per workgroup of the small-batch cosine kernel.
+constexpr int kCosSliceRows = 32;
 // 16-byte pieces per lane of the bf16 dot kernel for Hc (Hc % 8 == 0); 0 if
 // Hc is too large.
 int bf16_nv_for(int Hc);

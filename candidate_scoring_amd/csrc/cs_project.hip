@@ -21,13 +21,16 @@
 //    proj_cos_mfma otherwise) computes, per question, the tile
 //    C' = X Wc^T (255 x P, X [K][Hc]) with v_mfma_f32_32x32x16_bf16, keeps it
 //    in registers, and reduces each row to (c'.q', |c'|^2) in its epilogue;
-//    the projected candidates never reach global memory.
+//    the projected candidates never reach global memory. Small batches use
+//    proj_cos_slice instead: one workgroup per 32 candidates, the slices of
+//    a question merged like the split scoring kernels.
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "cs_device.h"
 #include "cs_launch.h"
@@ -878,6 +881,151 @@ __global__ __launch_bounds__(512) void proj_cos_mfma(KernelArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Cosine for small batches (B * ceil(K / 32) workgroups fit the compute
+// units): one workgroup per 32-candidate slice of a question, so a single
+// question is spread over up to eight compute units instead of one. Eight
+// waves share the slice's 32 x P tile C' = X Wc^T: wave w owns the 32-feature
+// block w when it exists (P = 64 * TN has 2 * TN of them). The hidden
+// dimension moves through two LDS buffers 64 bf16 at a time, with the loads
+// of the next kCosSliceAhead chunks in flight in registers (all of a
+// 512-wide hidden size in one round); loads past the last chunk repeat it
+// and hidden positions past Hc are zeroed in the deposit, so every lane
+// issues the same loads. Each row is reduced to (c'.q', |c'|^2) in registers, the waves'
+// parts are added in wave order, and the slice's softmax partial is merged
+// with the question's other slices by the last to finish.
+constexpr int kCosSliceWaves = 8;
+constexpr int kCosSliceAhead = 8;
+
+template <int TN>
+__global__ __launch_bounds__(kCosSliceWaves * kWave) void proj_cos_slice(
+    KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
+    const float* __restrict__ qp) {
+  constexpr int kThreads = kCosSliceWaves * kWave;
+  constexpr int P = 64 * TN;
+  constexpr int kRows = kCosSliceRows;
+  constexpr int kWPer = P * 8 / kThreads;  // W pieces per thread per chunk
+  static_assert(kRows * 8 == 256 && kWPer == TN, "X pieces of a chunk: one per thread of 256");
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][kRows * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][P * kRowStride];
+  __shared__ float qs[256];
+  __shared__ float red[kCosSliceWaves][kRows][2];
+  __shared__ Lds s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int H = a.D, K = a.K;
+  const int b = (int)blockIdx.x / a.G, g = (int)blockIdx.x % a.G;
+  const int r0 = g * kRows, n = min(kRows, K - r0);
+  const uint16_t* Xs = xc + ((size_t)b * (size_t)K + (size_t)r0) * (size_t)H;
+  const int nchunks = (H + kChunk - 1) / kChunk;
+  // q' is needed only after the contraction: held in a register until then,
+  // so the chunk loads do not wait behind it.
+  const float qv = qp[(size_t)b * P + min(tid & 255, P - 1)];
+  // This thread's pieces of a chunk: row (tid % 256) / 8 of X (clamped to
+  // the slice's last row; the upper 256 threads load the same pieces and
+  // do not deposit them) and rows tid / 8 + 64 i of W, hidden piece tid % 8.
+  const int pc = tid & 7, xrow = min((tid & 255) >> 3, n - 1);
+  auto fetch = [&](int c, uint4& px, uint4 (&pw)[kWPer]) {
+    const int h = min(c * kChunk + 8 * pc, H - 8);
+    px = load_piece<false>(Xs + (size_t)xrow * (size_t)H + h);
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i)
+      pw[i] = load_piece<false>(wc + (size_t)((tid >> 3) + 64 * i) * (size_t)H + h);
+  };
+  auto deposit = [&](int buf, int c, const uint4& px, const uint4 (&pw)[kWPer]) {
+    const uint32_t keep = c * kChunk + 8 * pc < H ? ~0u : 0u;
+    if (tid < 256)  // uniform across the wave
+      *reinterpret_cast<uint4*>(&sX[buf][(tid >> 3) * kRowStride + 8 * pc]) =
+          make_uint4(px.x & keep, px.y & keep, px.z & keep, px.w & keep);
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i)
+      *reinterpret_cast<uint4*>(&sW[buf][((tid >> 3) + 64 * i) * kRowStride + 8 * pc]) =
+          make_uint4(pw[i].x & keep, pw[i].y & keep, pw[i].z & keep, pw[i].w & keep);
+  };
+  uint4 px[kCosSliceAhead], pw[kCosSliceAhead][kWPer];
+#pragma unroll
+  for (int i = 0; i < kCosSliceAhead; ++i) fetch(min(i, nchunks - 1), px[i], pw[i]);
+  // A block past the tile (TN < 4) is still multiplied, on a clamped W row,
+  // so the matrix instructions need no branch; the epilogue drops it.
+  const int wrow = min(32 * wave + (lane & 31), P - 1);
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  // A group of kCosSliceAhead chunks. With another group to come, each
+  // chunk's registers are refilled with the chunk kCosSliceAhead later as
+  // soon as it sits in LDS; the last group issues no loads (so none is left
+  // in flight for the epilogue to wait on) and stops at the last chunk.
+  auto group = [&](auto refill, int c0) {
+    constexpr bool kRefill = decltype(refill)::value;
+#pragma unroll
+    for (int i = 0; i < kCosSliceAhead; ++i) {
+      const int c = c0 + i, buf = i & 1;
+      if (!kRefill && c >= nchunks) break;  // uniform (scalar)
+      // Buffer buf was last read for chunk c - 2, which every wave finished
+      // before the previous barrier.
+      deposit(buf, c, px[i], pw[i]);
+      __syncthreads();
+      if (kRefill) fetch(min(c + kCosSliceAhead, nchunks - 1), px[i], pw[i]);
+#pragma unroll
+      for (int ks = 0; ks < kChunk / 16; ++ks) {
+        // Lane l feeds row/column l % 32 and hidden elements 8*(l/32) .. +8
+        // of this 16-wide step, the same slots for both operands.
+        const int kofs = 16 * ks + 8 * (lane >> 5);
+        const bf16x8_t af =
+            *reinterpret_cast<const bf16x8_t*>(&sX[buf][(lane & 31) * kRowStride + kofs]);
+        const bf16x8_t bw =
+            *reinterpret_cast<const bf16x8_t*>(&sW[buf][wrow * kRowStride + kofs]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
+      }
+    }
+  };
+  int c0 = 0;
+  for (; c0 + kCosSliceAhead < nchunks; c0 += kCosSliceAhead)
+    group(std::integral_constant<bool, true>(), c0);
+  group(std::integral_constant<bool, false>(), c0);
+  if (tid < 256) qs[tid] = tid < P ? qv : 0.0f;
+  __syncthreads();
+  // Accumulator e of lane l: row 8*(e/4) + 4*(l/32) + e%4 of the slice,
+  // feature 32*wave + l%32.
+  const bool own = wave < 2 * TN;
+  const float qf = qs[(32 * wave + (lane & 31)) & 255];
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float x = own ? acc[e] : 0.0f;
+    v[e] = x * qf;
+    v[16 + e] = x * x;
+  }
+  // Lane l ends with value l % 32 of its half: a dot (< 16) or a squared
+  // norm (>= 16) of accumulator element l % 16.
+  const float tot = halfwave_reduce_transposed<32>(v, lane, OpSum());
+  {
+    const int idx = lane & 31, e = idx & 15;
+    red[wave][8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][idx >> 4] = tot;
+  }
+  __syncthreads();
+  if (tid < 2 * kRows) {
+    const int row = tid >> 1, kind = tid & 1;
+    float sum = red[0][row][kind];
+#pragma unroll
+    for (int w = 1; w < kCosSliceWaves; ++w) sum += red[w][row][kind];
+    if (kind == 0)
+      s.dot[row] = sum;
+    else
+      s.ss[row] = sum;
+  }
+  __syncthreads();
+  const Question qn{(size_t)b * (size_t)K, K};
+  if (wave == 0) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qq = fmaf(qs[lane + kWave * i], qs[lane + kWave * i], qq);
+    qq = wave_allreduce(qq, lane, OpSum());
+    const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
+    slice_softmax<true>(s, a, qn, b, g, r0, n, zfac, lane);
+  }
+  if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+}
+
+// ---------------------------------------------------------------------------
 // The same cosine tile with asynchronous staging (Hc % 64 == 0): the hidden
 // dimension moves through two LDS stages of 64 bf16 per row, filled by
 // global_load_lds_dwordx4 (no staging registers): one chunk is in flight
@@ -1262,6 +1410,18 @@ void launch_cos_tile(const KernelArgs& a, const ProjArgs& p, unsigned grid, hipS
 
 template <bool NT>
 hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t stream) {
+  if (p.cos_slice) {
+    // Small batch: B * G workgroups (at most one per compute unit).
+    const dim3 grid((unsigned)(p.B * p.G)), block(kCosSliceWaves * kWave);
+    switch (p.P / 64) {
+      case 1: hipLaunchKernelGGL(proj_cos_slice<1>, grid, block, 0, stream, a, p.xc, p.wc, p.qp); break;
+      case 2: hipLaunchKernelGGL(proj_cos_slice<2>, grid, block, 0, stream, a, p.xc, p.wc, p.qp); break;
+      case 3: hipLaunchKernelGGL(proj_cos_slice<3>, grid, block, 0, stream, a, p.xc, p.wc, p.qp); break;
+      case 4: hipLaunchKernelGGL(proj_cos_slice<4>, grid, block, 0, stream, a, p.xc, p.wc, p.qp); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)std::min(p.B, 1 << 20);
   switch (p.P / 64) {
     case 1: launch_cos_tile<1, NT>(a, p, grid, stream); break;
@@ -1292,39 +1452,31 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.B = p.B;
   a.K = p.K;
   a.D = p.Hc;
-  a.G = p.cosine ? 1 : p.G;
-  a.rpg = (p.K + a.G - 1) / a.G;
+  a.G = p.G;
+  a.rpg = p.cosine ? kCosSliceRows : (p.K + p.G - 1) / p.G;
   a.tickets = a.G > 1 ? p.tickets : nullptr;
   a.partials = a.G > 1 ? p.partials : nullptr;
   a.zscale = p.zscale;
   a.cosine = p.cosine;
-  if (!p.cosine && p.B <= kGemvMaxB) {
-    // A handful of questions: q' and u as matrix-vector products from the
-    // heads' own layout (no packing); the candidate pass is unchanged.
+  const bool few = p.B <= kGemvMaxB;
+  if (few) {
+    // A handful of questions: q' as matrix-vector products from Wq's own
+    // layout (and, for dot, u from Wc's, with no packing).
     const unsigned qgroups = (unsigned)((p.P + 3) / 4);
-    const unsigned fgroups = (unsigned)((p.Hc / 8 + kFoldGemvPieces - 1) / kFoldGemvPieces);
-    auto launch = [&](auto query, auto fold) {
+    auto launch = [&](auto query) {
       hipLaunchKernelGGL(query, dim3(qgroups), dim3(256), 0, stream, p.xq, p.wq, p.qp, p.B, p.Hq,
                          p.P, a.tickets);
-      hipLaunchKernelGGL(fold, dim3(fgroups), dim3(256), 0, stream, p.qp, p.wc, p.u, p.B, p.Hc,
-                         p.P);
     };
-    if (p.B == 1) launch(proj_query_gemv<1>, fold_query_gemv<1>);
-    else if (p.B == 2) launch(proj_query_gemv<2>, fold_query_gemv<2>);
-    else launch(proj_query_gemv<4>, fold_query_gemv<4>);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int nv = bf16_nv_for(p.Hc);
-    return p.nt ? launch_bf16_dot<true>(a, p, nv, stream) : launch_bf16_dot<false>(a, p, nv, stream);
-  }
-  // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
-  {
+    if (p.B == 1) launch(proj_query_gemv<1>);
+    else if (p.B == 2) launch(proj_query_gemv<2>);
+    else launch(proj_query_gemv<4>);
+  } else {
+    // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
     const long long tiles = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
     // Dot also packs Wc^T in this launch: at least one workgroup per compute
     // unit, so that a small batch does not pack it on a few of them.
     const long long cus = p.compute_units > 0 ? p.compute_units : 256;
     const long long groups = p.cosine ? tiles : std::max(tiles, cus);
-    // For dot the same launch also packs Wc^T for the fold.
     // Blocks in flight per wave: every whole block of a wave's share up to
     // ten (more take further rounds), so short hidden sizes issue no
     // repeated loads.
@@ -1332,8 +1484,7 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
     auto launch = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kPqWaves * kWave), 0, stream, p.xq,
                          p.wq, p.qp, p.cosine ? nullptr : p.parts, p.B, p.Hq, p.P, p.wc,
-                         p.cosine ? nullptr : p.wpack, p.Hc,
-                         p.cosine || p.G <= 1 ? nullptr : p.tickets, tiles);
+                         p.cosine ? nullptr : p.wpack, p.Hc, a.tickets, tiles);
     };
     if (per_wave <= 1) launch(proj_query_mfma<1>);
     else if (per_wave <= 2) launch(proj_query_mfma<2>);
@@ -1344,9 +1495,18 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.cosine) return p.nt ? launch_cos_mfma<true>(a, p, stream) : launch_cos_mfma<false>(a, p, stream);
-  // u = Wc^T q' (one wave per 32 questions x 128 h), then one
-  // bandwidth-bound pass over the candidates.
-  {
+  // u = Wc^T q', then one bandwidth-bound pass over the candidates.
+  if (few) {
+    const unsigned fgroups = (unsigned)((p.Hc / 8 + kFoldGemvPieces - 1) / kFoldGemvPieces);
+    auto launch = [&](auto fold) {
+      hipLaunchKernelGGL(fold, dim3(fgroups), dim3(256), 0, stream, p.qp, p.wc, p.u, p.B, p.Hc,
+                         p.P);
+    };
+    if (p.B == 1) launch(fold_query_gemv<1>);
+    else if (p.B == 2) launch(fold_query_gemv<2>);
+    else launch(fold_query_gemv<4>);
+  } else {
+    // One wave per 32 questions x 128 h.
     const long long tiles =
         (long long)((p.B + 31) / 32) * ((p.Hc + 32 * kFoldNb - 1) / (32 * kFoldNb));
     const long long cus = p.compute_units > 0 ? p.compute_units : 256;

@@ -173,11 +173,11 @@ int cs_score_candidates_ragged(const float *queries, const float *candidates,
  * for cosine, each question's projected candidates are computed on the
  * matrix cores and reduced to their similarity in registers. The workspace
  * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected
- * queries and, for dot, the folded queries, an exact three-part bf16 split
- * of the projected ones and Wc^T, both in matrix-core fragment order, and
- * the merge state of the candidate pass, which a small batch spreads over
- * several workgroups per question; its contents are scratch between calls
- * (the call initialises what it needs). Implemented shapes: Hq and Hc multiples of 8, P <= 256,
+ * queries, the merge state of the candidate pass (which a small batch
+ * spreads over several workgroups per question) and, for dot, the folded
+ * queries, an exact three-part bf16 split of the projected ones and Wc^T,
+ * both in matrix-core fragment order; its contents are scratch between
+ * calls (the call initialises what it needs). Implemented shapes: Hq and Hc multiples of 8, P <= 256,
  * 16-byte aligned inputs, P a multiple of 64 for cosine, Hc <= 4096 for dot;
  * other valid sizes return CS_ERR_UNSUPPORTED. Enqueues two (cosine) or
  * three (dot) kernels on `stream`. */

@@ -82,7 +82,8 @@ def _bits(b, dev):
 
 
 @pytest.mark.parametrize("kind", ["ragged", "projected_dot", "projected_cosine",
-                                  "projected_dot_split", "projected_dot_split_tiles"])
+                                  "projected_dot_split", "projected_dot_split_tiles",
+                                  "projected_cosine_slices"])
 def test_capture_multi_kernel_paths_replay_exact(cs, kind):
     """The ragged and projection entry points captured into a graph (through
     torch's capture of the current stream) replay to exactly the direct
@@ -106,7 +107,7 @@ def test_capture_multi_kernel_paths_replay_exact(cs, kind):
 
         shape = (rows,)
     else:
-        sim = "cosine" if kind == "projected_cosine" else "dot"
+        sim = "cosine" if kind.startswith("projected_cosine") else "dot"
         if kind == "projected_dot_split":
             # Two questions of 1.3 MB: the candidate pass is split, merged
             # through tickets the query projection clears in the same graph
@@ -115,6 +116,10 @@ def test_capture_multi_kernel_paths_replay_exact(cs, kind):
         elif kind == "projected_dot_split_tiles":
             # Six questions: the same split behind the matrix-core query side.
             w = workloads.projected_inputs(75, 6, 255, 2560, 2560, 256, sim)
+        elif kind == "projected_cosine_slices":
+            # Two questions of 255 candidates, 32 per workgroup, merged
+            # through the tickets.
+            w = workloads.projected_inputs(76, 2, 255, 512, 512, 256, sim)
         else:
             w = workloads.projected_inputs(73, 300, 40, 136, 256, 128, sim)
         xq, xc = _bits(w.xq_bits, dev), _bits(w.xc_bits, dev)

@@ -71,18 +71,18 @@ def dev(cs):
     (2, 64, 128, 1000, 192, "cosine"),
     (5, 5, 64, 24, 64, "cosine"),
     (2, 1, 64, 64, 64, "cosine"),
-    (2, 130, 64, 32, 128, "cosine"),       # hidden below one 64-wide chunk
-    (3, 255, 64, 96, 192, "cosine"),       # hidden not a multiple of 64: staged in registers
-    (2, 255, 64, 64, 256, "cosine"),       # one chunk of the DMA ring
-    (3, 255, 64, 192, 192, "cosine"),      # three chunks: the ring restarts per question
-    (2, 200, 64, 320, 256, "cosine"),      # five chunks
+    (2, 130, 64, 32, 128, "cosine"),       # hidden below one 64-wide chunk, a partial slice
+    (3, 255, 64, 96, 192, "cosine"),       # hidden not a multiple of 64: a zeroed tail
+    (2, 255, 64, 64, 256, "cosine"),       # one 64-wide chunk
+    (3, 255, 64, 192, 192, "cosine"),      # three chunks: one group of four in flight
+    (2, 200, 64, 320, 256, "cosine"),      # five chunks: a second group
     (3, 17, 64, 2048, 64, "cosine"),
     (3, 77, 520, 1000, 96, "dot"),
     (2, 255, 8, 8, 8, "dot"),
     (2, 100, 136, 4096, 256, "dot"),
     (3, 255, 64, 2048, 64, "dot"),         # four 16-byte pieces per lane
     (2, 50, 520, 1000, 200, "dot"),        # P not a multiple of 16 or 32
-    (1, 255, 4096, 4096, 256, "cosine"),   # one question, 64 chunks of the DMA ring
+    (1, 255, 4096, 4096, 256, "cosine"),   # one question over eight slices, 64 chunks
     (1, 255, 2560, 2560, 256, "dot"),      # one question: the candidate pass is split
     (2, 200, 512, 1000, 96, "dot"),        # split, a partial last slice
     (200, 40, 256, 2048, 128, "dot"),      # 7 question blocks: the fold's four-wave tiles
@@ -90,6 +90,12 @@ def dev(cs):
     (4, 60, 1032, 72, 256, "dot"),         # matrix-vector query side: a partial head row
                                            # chunk, a partial column strip of the fold
     (3, 33, 4104, 136, 250, "dot"),        # three chunks per head row, P < 256 clamped rows
+    (7, 32, 64, 136, 128, "cosine"),       # one whole 32-candidate slice
+    (9, 33, 64, 200, 192, "cosine"),       # a second slice of one candidate
+    (8, 250, 64, 128, 64, "cosine"),       # 8 x 8 slices: the most split questions take
+    (9, 250, 64, 128, 64, "cosine"),       # one question more: the tile kernel
+    (256, 32, 64, 136, 64, "cosine"),      # unsplit questions: one workgroup per compute unit
+    (257, 32, 64, 136, 64, "cosine"),      # one question more: the tile kernel
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
@@ -100,6 +106,8 @@ def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
 @pytest.mark.parametrize("B,K,Hc,P", [
     (600, 33, 256, 128),   # even chunk count: the ring runs across questions
     (300, 40, 192, 64),    # three chunks: the ring restarts for every question
+    (270, 10, 64, 256),    # one chunk of the ring
+    (270, 12, 96, 64),     # hidden not a multiple of 64: the register-staged tile
 ])
 def test_projected_cosine_many_questions(cs, orc, dev, B, K, Hc, P):
     """More questions than compute units, so a workgroup of the cosine kernel
@@ -155,25 +163,29 @@ def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
     check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
 
 
-@pytest.mark.parametrize("B", [3, 6])  # matrix-vector / matrix-core query side
-def test_projected_split_on_an_unprepared_workspace(cs, orc, dev, B):
-    """A small dot batch spreads each question's candidate pass over several
-    workgroups, merged through tickets in the workspace; the query projection
-    clears them, so a workspace full of garbage (and then the one a previous
-    call left) gives the same correct result."""
+@pytest.mark.parametrize("B,sim", [(3, "dot"), (6, "dot"), (2, "cosine")])
+def test_projected_split_on_an_unprepared_workspace(cs, orc, dev, B, sim):
+    """A small batch spreads each question's candidate pass over several
+    workgroups (dot: behind the matrix-vector and the matrix-core query side;
+    cosine: 32 candidates per workgroup), merged through tickets in the
+    workspace; the query projection clears them, so a workspace full of
+    garbage (and then the one a previous call left) gives the same correct
+    result."""
     import torch
 
-    w = workloads.projected_inputs(151 + B, B, 255, 2560, 2560, 256, "dot")
-    assert cs.cs_plan_groups(B, 255, 1280, "dot", True) > 1  # the same bytes per question
+    H = 2560 if sim == "dot" else 512
+    w = workloads.projected_inputs(151 + B, B, 255, H, H, 256, sim)
+    if sim == "dot":
+        assert cs.cs_plan_groups(B, 255, 1280, "dot", True) > 1  # the same bytes per question
     xq, xc = to_dev16(w.xq_bits, dev), to_dev16(w.xc_bits, dev)
     wq, wc = to_dev16(w.wq_bits, dev), to_dev16(w.wc_bits, dev)
-    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, "dot")
+    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, sim)
     ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
     ref = want(orc, w)
-    note(f"case projected split B={B}, workspace of 0xFF bytes, two calls")
+    note(f"case projected split B={B} {sim}, workspace of 0xFF bytes, two calls")
     for call in range(2):
         out = torch.full((w.B, w.K), -3.0, device=dev)
-        st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, "dot",
+        st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, sim,
                                    float(w.scale), 1.0, out, ws, nbytes)
         assert st == 0, st
         torch.cuda.synchronize()
