@@ -14,7 +14,7 @@
 //    u = Wc^T q' [B][Hc], and fused_bf16_dot streams the bf16 candidate rows once against
 //    u, with the same in-workgroup softmax as the plain scoring kernels. The
 //    candidate side stays a bandwidth-bound pass; no candidate is projected.
-//    For four questions or fewer, proj_query_gemv and fold_query_gemv make
+//    For eight questions or fewer, proj_query_gemv and fold_query_gemv make
 //    q' and u as matrix-vector products from the heads' own layout instead.
 //  * cosine (CLM): the norm |Wc x_k| needs the projected rows, a dense
 //    contraction: proj_cos_mfma_async (hidden sizes in whole 64-wide chunks;
@@ -519,7 +519,7 @@ static_assert(kFoldNb == kFoldSplitWaves, "one column block per wave in the spli
 // matrix-vector products straight from their row-major layout, each reading
 // its head once with fp32 accumulation (the bf16 x bf16 products are exact).
 
-constexpr int kGemvMaxB = 4;
+constexpr int kGemvMaxB = 8;
 constexpr int kGemvUnroll = 4;  // 512-wide chunks of a head row in flight per wave
 
 // 8 bf16 times 8 bf16, widened exactly and accumulated in order.
@@ -643,9 +643,11 @@ __global__ __launch_bounds__(256) void fold_query_gemv(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) red[b][j][ph][pc] = acc[b][j];
   __syncthreads();
-  // Thread t sums column 8 * (t % 8) + (t / 8) % 8 of question t / 64.
-  const int b = tid / 64, j = (tid / kFoldGemvPieces) % 8, c = tid % kFoldGemvPieces;
-  if (b < NB) {
+  // Output o (threads take o = t, t + 256, ...) is column 8 * (o % 8) +
+  // (o / 8) % 8 of question o / 64.
+#pragma unroll
+  for (int o = tid; o < NB * 64; o += 256) {
+    const int b = o / 64, j = (o / kFoldGemvPieces) % 8, c = o % kFoldGemvPieces;
     float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < kFoldGemvPhases; ++r) sum += red[b][j][r][c];
@@ -1460,7 +1462,7 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
   a.cosine = p.cosine;
   const bool few = p.B <= kGemvMaxB;
   if (few) {
-    // A handful of questions: q' as matrix-vector products from Wq's own
+    // At most eight questions: q' as matrix-vector products from Wq's own
     // layout (and, for dot, u from Wc's, with no packing).
     const unsigned qgroups = (unsigned)((p.P + 3) / 4);
     auto launch = [&](auto query) {
@@ -1469,7 +1471,8 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
     };
     if (p.B == 1) launch(proj_query_gemv<1>);
     else if (p.B == 2) launch(proj_query_gemv<2>);
-    else launch(proj_query_gemv<4>);
+    else if (p.B <= 4) launch(proj_query_gemv<4>);
+    else launch(proj_query_gemv<8>);
   } else {
     // q' = Wq x_q for every question: one workgroup per 32 x 32 tile.
     const long long tiles = (long long)((p.B + 31) / 32) * ((p.P + 31) / 32);
@@ -1504,7 +1507,8 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
     };
     if (p.B == 1) launch(fold_query_gemv<1>);
     else if (p.B == 2) launch(fold_query_gemv<2>);
-    else launch(fold_query_gemv<4>);
+    else if (p.B <= 4) launch(fold_query_gemv<4>);
+    else launch(fold_query_gemv<8>);
   } else {
     // One wave per 32 questions x 128 h.
     const long long tiles =

@@ -114,8 +114,8 @@ def test_capture_multi_kernel_paths_replay_exact(cs, kind):
             # (matrix-vector query side).
             w = workloads.projected_inputs(74, 2, 255, 2560, 2560, 256, sim)
         elif kind == "projected_dot_split_tiles":
-            # Six questions: the same split behind the matrix-core query side.
-            w = workloads.projected_inputs(75, 6, 255, 2560, 2560, 256, sim)
+            # Ten questions: the same split behind the matrix-core query side.
+            w = workloads.projected_inputs(75, 10, 255, 2560, 2560, 256, sim)
         elif kind == "projected_cosine_slices":
             # Two questions of 255 candidates, 32 per workgroup, merged
             # through the tickets.

@@ -86,7 +86,9 @@ def dev(cs):
     (1, 255, 2560, 2560, 256, "dot"),      # one question: the candidate pass is split
     (2, 200, 512, 1000, 96, "dot"),        # split, a partial last slice
     (200, 40, 256, 2048, 128, "dot"),      # 7 question blocks: the fold's four-wave tiles
-    (5, 100, 520, 1000, 96, "dot"),        # one question past the matrix-vector query side
+    (5, 100, 520, 1000, 96, "dot"),        # eight-question matrix-vector kernels, three padded
+    (8, 40, 2056, 136, 128, "dot"),        # eight questions: the last on the matrix-vector side
+    (9, 100, 520, 1000, 96, "dot"),        # one question past the matrix-vector query side
     (4, 60, 1032, 72, 256, "dot"),         # matrix-vector query side: a partial head row
                                            # chunk, a partial column strip of the fold
     (3, 33, 4104, 136, 250, "dot"),        # three chunks per head row, P < 256 clamped rows
@@ -163,7 +165,7 @@ def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
     check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
 
 
-@pytest.mark.parametrize("B,sim", [(3, "dot"), (6, "dot"), (2, "cosine")])
+@pytest.mark.parametrize("B,sim", [(3, "dot"), (10, "dot"), (2, "cosine")])
 def test_projected_split_on_an_unprepared_workspace(cs, orc, dev, B, sim):
     """A small batch spreads each question's candidate pass over several
     workgroups (dot: behind the matrix-vector and the matrix-core query side;
