@@ -452,6 +452,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-ab", action="store_true", help="skip the fused vs unfused table")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch")
+    ap.add_argument("--projected-latency", action="store_true",
+                    help="time the one-question projected calls even with --no-latency")
     ap.add_argument("--no-projected", action="store_true",
                     help="skip the projection + scoring workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -540,7 +542,8 @@ def main():
     if not args.no_ragged:
         result["ragged"] = ragged_section(devc)
     if not args.no_projected:
-        result["projected"] = projected_section(devc, one_question=not args.no_latency)
+        result["projected"] = projected_section(
+            devc, one_question=args.projected_latency or not args.no_latency)
     if not args.no_cpu:
         log("cpu baseline: oracle on the headline batch")
         result["cpu_baseline"] = cpu_baseline(w)
