@@ -1374,9 +1374,11 @@ hipError_t launch_bf16_dot(const KernelArgs& a, const ProjArgs& p, int nv, hipSt
   const int R = bf16_rows_per_wave(nv);
   // Four waves per question: at 127 registers a CU holds four such
   // workgroups, so a 1024-question batch is resident at once (eight-wave
-  // workgroups ran in two rounds and measured about 1 % slower).
+  // workgroups ran in two rounds and measured about 1 % slower). A split
+  // batch has at most one slice per compute unit, so its slices take eight
+  // waves: twice the loads in flight on each unit.
   const int rpg = (p.K + p.G - 1) / p.G;
-  const int waves = std::max(1, std::min(4, (rpg + R - 1) / R));
+  const int waves = std::max(1, std::min(p.G > 1 ? 8 : 4, (rpg + R - 1) / R));
   const unsigned grid = (unsigned)std::min<long long>((long long)p.B * p.G, 1 << 20);
   const unsigned block = (unsigned)(waves * kWave);
   switch (nv) {
