@@ -455,6 +455,12 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
     const int k = tid + (int)blockDim.x * i;
     if (k < qn.K) out[k] = ek[i] * s.merge[k / a.rpg];
   }
+  // Return this question's part of the workspace to zero: its G partials
+  // (read above, before the barrier) and its ticket. The ticket array's
+  // length depends on B, so a later call with more questions finds its
+  // tickets where this call kept partials; those must read as zero.
+  for (int g = tid; g < a.G; g += (int)blockDim.x)
+    a.partials[(size_t)b * a.G + g] = make_float2(0.0f, 0.0f);
   if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -207,7 +207,45 @@ def test_output_canaries_and_workspace_left_zero(cs, orc, dev):
         assert torch.all(buf[:pad] == -123.0) and torch.all(buf[pad + B * K:] == -123.0)
         tickets = wsv[: 4 * B].view(torch.int32)
         assert torch.all(tickets == 0), tickets
+        # tickets and slice partials alike: the whole workspace is zero again
+        assert torch.all(wsv == 0), int(torch.count_nonzero(wsv))
         assert torch.all(ws[:pad] == 0) and torch.all(ws[pad + nbytes:] == 0)
+
+
+def test_workspace_reused_by_a_larger_batch(cs, orc, dev):
+    """A split call leaves its whole workspace zero, so a later call with
+    more questions on the same (cached) workspace, whose tickets then sit
+    where the first call kept its slice partials, still merges correctly."""
+    import torch
+
+    K, D = 255, 2560
+    first = workloads.normal_inputs(41, 1, K, D)
+    second = workloads.normal_inputs(43, 100, K, D)
+    g1 = cs.cs_plan_groups(1, K, D, "dot", True)
+    g2 = cs.cs_plan_groups(100, K, D, "dot", True)
+    note(f"case reuse: B=1 ({g1} slices) then B=100 ({g2} slices) on one workspace")
+    assert g1 > 1 and g2 > 1
+    # the second call's tickets overlap the first call's partials
+    assert cs.cs_workspace_bytes_for_groups(100, g2) > 256 + 8 * g1
+    nbytes = max(cs.cs_workspace_bytes(1, K, D, "dot"), cs.cs_workspace_bytes(100, K, D, "dot"))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for Q, C in (first, second):
+            B = Q.shape[0]
+            q, c = to_dev(Q, dev), to_dev(C, dev)
+            out = torch.empty(B, K, dtype=torch.float32, device=dev)
+            st = cs.cs_score_candidates_batch(q, c, B, K, D, "dot", 0.0625, 1.0, out, ws, nbytes)
+            assert st == 0
+            torch.cuda.synchronize()
+            want = orc.score(Q, C, "dot", 0.0625)
+            check(out.cpu().numpy(), want, f"reuse rep={rep} B={B}")
+            assert torch.all(ws == 0), int(torch.count_nonzero(ws))
+    # the Python wrapper's cached workspace, same order
+    for Q, C in (first, second):
+        q, c = to_dev(Q, dev), to_dev(C, dev)
+        out = cs.score(q, c, "dot", 0.0625, 1.0)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), orc.score(Q, C, "dot", 0.0625), f"wrapper B={Q.shape[0]}")
 
 
 def test_rejections_leave_device_output_untouched(cs, dev):
