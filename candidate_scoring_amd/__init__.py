@@ -38,6 +38,7 @@ CS_ERR_WORKSPACE = -8
 CS_ERR_LAUNCH = -9
 CS_ERR_HOST_POINTER = -10
 CS_ERR_UNSUPPORTED = -11
+CS_NOALLOC_SCRATCH_BYTES = 64 * 1024
 
 _lib = None
 _bench = None
@@ -74,6 +75,8 @@ def load(path: Path | str = LIBRARY):
         "cs_score_candidates_batch": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
         "cs_score_candidates_batch_groups": (
             i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, i32, vp]),
+        "cs_score_candidates_batch_noalloc": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp,
+                                                    vp]),
         "cs_score_candidates_unfused": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp]),
         "cs_projected_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "cs_score_projected": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp,
@@ -220,6 +223,14 @@ def cs_score_candidates_batch_groups(queries, candidates, B: int, K: int, D: int
     return load().cs_score_candidates_batch_groups(
         _ptr(queries), _ptr(candidates), B, K, D, _sim(similarity), scale, temperature,
         _ptr(out), _ptr(workspace), workspace_bytes, groups, _stream(stream))
+
+
+def cs_score_candidates_batch_noalloc(queries, candidates, B: int, K: int, D: int, similarity,
+                                      scale: float, temperature: float, out,
+                                      stream=None) -> int:
+    return load().cs_score_candidates_batch_noalloc(_ptr(queries), _ptr(candidates), B, K, D,
+                                                    _sim(similarity), scale, temperature,
+                                                    _ptr(out), _stream(stream))
 
 
 def cs_score_candidates_unfused(queries, candidates, B: int, K: int, D: int, similarity,

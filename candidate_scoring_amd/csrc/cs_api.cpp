@@ -504,6 +504,28 @@ int cs_score_candidates_batch(const float* queries, const float* candidates, int
                workspace_bytes, G, stream);
 }
 
+int cs_score_candidates_batch_noalloc(const float* queries, const float* candidates, int B,
+                                      int K, int D, int similarity, float scale,
+                                      float temperature, float* out, hipStream_t stream) {
+  int st = validate(queries, candidates, out, B, K, D, similarity, scale, temperature);
+  if (st != CS_OK) return st;
+  static_assert(cs::kStaticScratchBytes == CS_NOALLOC_SCRATCH_BYTES, "one scratch size");
+  const int G = plan_groups(B, K, D);
+  if (G <= 1)  // one workgroup per question: no workspace at all
+    return score(queries, candidates, B, K, D, similarity, scale, temperature, out, nullptr, 0,
+                 1, stream);
+  const size_t need = workspace_for(B, G);
+  if (need > cs::kStaticScratchBytes) return CS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t err = cs::static_scratch(&ws, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return CS_ERR_LAUNCH;
+  }
+  return score(queries, candidates, B, K, D, similarity, scale, temperature, out, ws, need, G,
+               stream);
+}
+
 int cs_score_candidates_unfused(const float* queries, const float* candidates, int B, int K,
                                 int D, int similarity, float scale, float temperature,
                                 float* out, float* row_norms, hipStream_t stream) {

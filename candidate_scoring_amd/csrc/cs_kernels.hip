@@ -47,10 +47,21 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "cs_device.h"
 #include "cs_launch.h"
+
+// Split-path workspace of the entry point that allocates nothing: one copy
+// per GPU, held until the process ends. In host code this name is only a
+// stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress (static_scratch below) and is the only form passed to
+// kernels or copies. Every call leaves it zero again (the last slice of a
+// question clears its ticket and partials), so it is cleared only once per
+// device, before its first use.
+static __device__ __align__(256) unsigned char scratch[cs::kStaticScratchBytes];
 
 namespace cs {
 namespace {
@@ -401,6 +412,34 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
   if (tail > 0)
     hipLaunchKernelGGL(zero_bytes, dim3(1), dim3(64), 0, stream, base + head + words * 4, tail);
   return hipGetLastError();
+}
+
+// Device address of this GPU's `scratch` array, looked up once per device
+// with that device current, and cleared by a fill kernel enqueued on
+// `stream` ahead of its first use (no memset node, no synchronization).
+hipError_t static_scratch(void** ptr, hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex setup;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(setup);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return err;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      err = launch_zero(p, kStaticScratchBytes, stream);
+      if (err != hipSuccess) return err;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace cs

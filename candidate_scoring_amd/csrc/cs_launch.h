@@ -73,6 +73,12 @@ int bf16_nv_for(int Hc);
 int bf16_rows_per_wave(int nv);
 hipError_t launch_projected(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+// Bytes of the per-GPU static split workspace of the entry point that
+// allocates nothing (equal to CS_NOALLOC_SCRATCH_BYTES of the C ABI).
+constexpr size_t kStaticScratchBytes = 64 * 1024;
+// Device address of the current GPU's static split workspace; the first
+// call on a device looks it up and enqueues its clearing on `stream`.
+hipError_t static_scratch(void** ptr, hipStream_t stream);
 // Unfused baseline, first pass: norms[r] = |C row r| for r < rows.
 hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,
                             hipStream_t stream);

@@ -139,6 +139,25 @@ int cs_score_candidates_batch_groups(const float *queries, const float *candidat
                                      float temperature, float *out, void *workspace,
                                      size_t workspace_bytes, int groups, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call, plan and result as cs_score_candidates_batch() with a workspace of
+ * cs_workspace_bytes() bytes, but the split path's workspace is a static
+ * array of CS_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU,
+ * held until the process ends. Neither this call nor its set-up calls
+ * hipMalloc, hipFree or any allocating routine. The first call on each
+ * device looks up that device's array and enqueues one extra kernel on
+ * `stream` that clears it; every call leaves it zero again. All calls on one
+ * GPU share the array, so calls that may overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued. A plan whose
+ * workspace would exceed CS_NOALLOC_SCRATCH_BYTES returns CS_ERR_WORKSPACE
+ * (the planner never makes one: split plans hold at most one slice per
+ * compute unit). Errors and validation as cs_score_candidates_batch(). */
+#define CS_NOALLOC_SCRATCH_BYTES (64 * 1024)
+int cs_score_candidates_batch_noalloc(const float *queries, const float *candidates, int B,
+                                      int K, int D, int similarity, float scale,
+                                      float temperature, float *out, hipStream_t stream);
+
 /* Ragged batch: B questions with their own candidate counts, one launch.
  * Question b owns candidate rows offsets[b] .. offsets[b+1]-1 of
  * candidates [total_rows][D] and the same slots of out [total_rows];

@@ -105,6 +105,14 @@ def test_rejected_before_any_device_work(lib, case):
                                       args["similarity"], args["scale"], args["temperature"],
                                       args["out"], None, 0, None)
         assert st1 == CODE[expect]
+    # the entry point that allocates nothing validates the same way, before
+    # it looks up or clears its static workspace
+    st2 = lib.cs_score_candidates_batch_noalloc(args["query"], args["candidates"], args["B"],
+                                                args["K"], args["D"], args["similarity"],
+                                                args["scale"], args["temperature"], args["out"],
+                                                None)
+    assert st2 == CODE[expect], (origin, change, st2)
+    assert np.all(out == -7.0) and np.all(q == -7.0) and np.all(c == -7.0)
 
 
 def test_workspace_and_group_rejections(lib):
