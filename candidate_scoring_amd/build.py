@@ -67,11 +67,11 @@ def _run(cmd: list[str], verbose: bool) -> str:
 def spilling_kernels(remarks: str) -> list[tuple[str, int]]:
     """Kernels whose resource-usage remarks report scratch (spilled) memory.
 
-    The fragment reads of the matrix-core kernels are inline ds_read
-    instructions that the compiler does not track: a value it spilled or
-    copied between such a read and its explicit wait would be taken before
-    the data arrived. Every kernel of the library is therefore required to
-    run without scratch, and the build checks it.
+    Every kernel here is sized to keep its working set in registers: the
+    hot loops hold 16-byte loads in flight and the matrix-core tiles hold
+    their accumulators, and a spill would put scratch traffic into each
+    iteration. The build therefore fails when any kernel uses scratch, so
+    that a change which pushes one over its register budget is noticed.
     """
     out, name = [], None
     for line in remarks.splitlines():
@@ -98,8 +98,8 @@ def build(verbose: bool = False) -> list[Path]:
     spills = spilling_kernels(remarks)
     if spills:
         tmp.unlink(missing_ok=True)
-        raise RuntimeError("build: kernels use scratch memory (spills), which the untracked "
-                           "fragment reads do not allow: " + ", ".join(f"{n} ({b} B/lane)"
+        raise RuntimeError("build: kernels use scratch memory (spills), which this library "
+                           "does not allow: " + ", ".join(f"{n} ({b} B/lane)"
                                                                      for n, b in spills))
     tmp.replace(LIBRARY)
     tmpb = BENCH_LIBRARY.with_suffix(".so.tmp")

@@ -103,20 +103,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-
-// One 16-byte fragment read from LDS at byte address addr + OFF. Written as
-// inline assembly so that the compiler, which cannot always tell which DMA
-// a read depends on, does not add a wait for every DMA in flight; the
-// kernels' own vmcnt waits and barriers order the reads instead. The result
-// is not ready until an lgkmcnt(0) wait (lds_fragments_ready()).
-template <int OFF>
-__device__ __forceinline__ void lds_fragment(bf16x8_t& f, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
-}
 
 // Fragment-packed operand of v_mfma_f32_32x32x16_bf16: element (row, k) of
 // an R x Kd matrix, with nks = Kd / 16 steps, sits in fragment (row / 32,
@@ -1039,9 +1025,12 @@ __global__ __launch_bounds__(kCosSliceWaves * kWave) void proj_cos_slice(
 // fetches piece p ^ f(r) of that row (an XOR swizzle instead of padding),
 // and readers undo it.
 //
-// The fragment reads are inline assembly that the compiler does not track, so
-// it adds no wait for the DMAs in flight; the ring's explicit vmcnt waits and
-// barriers order every read after the DMA that fills its stage.
+// Every stage of each operand is an LDS object of its own, and the fragment
+// reads are ordinary loads. The compiler tracks which LDS object a DMA in
+// flight writes, so a read from one stage does not wait for the refill of the
+// other; where a read does depend on this wave's own DMA, the compiler's wait
+// covers it. The ring's explicit vmcnt waits and barriers add what the
+// compiler cannot see: that the other waves' DMAs into a stage have landed.
 constexpr int kAChunk = 64;                        // bf16 per row per stage
 constexpr int kAStages = 2;                        // 128 KiB of LDS
 constexpr int kARowBytes = 2 * kAChunk;            // 128
@@ -1050,15 +1039,20 @@ constexpr int kARowsPerLoad = 1024 / kARowBytes;   // 8 rows per DMA instruction
 constexpr int kATileBytes = 256 * kARowBytes;      // X or W tile of one stage: 32 KiB
 constexpr int kAKSteps = kAChunk / 16;             // 4 MFMA k-steps per chunk
 
-__shared__ __attribute__((aligned(1024))) uint8_t g_xs[kAStages][kATileBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_ws[kAStages][kATileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs0[kATileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs1[kATileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ws0[kATileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ws1[kATileBytes];
 __shared__ __attribute__((aligned(1024))) float g_qp[256];  // q' of the current question
 
 // X tile (W == false) or W tile (W == true) of stage S.
 template <int S, bool W>
 __device__ __forceinline__ uint8_t* stage_tile() {
   static_assert(S >= 0 && S < kAStages, "stage index");
-  return W ? g_ws[S] : g_xs[S];
+  if constexpr (S == 0)
+    return W ? g_ws0 : g_xs0;
+  else
+    return W ? g_ws1 : g_xs1;
 }
 
 // Workgroup barrier for the stage ring: this wave's LDS reads are complete
@@ -1106,26 +1100,14 @@ __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* w
   }
 }
 
-// Fragment reads of one 16-wide step: N 32-row blocks, 4 KiB apart, starting
-// at byte address addr (the offsets are immediates of the instruction).
+// Fragment reads of one 16-wide step: N 32-row blocks, 4 KiB apart, from
+// base (an address inside one stage tile).
 template <int N>
-__device__ __forceinline__ void lds_blocks(bf16x8_t (&f)[N], uint32_t addr) {
+__device__ __forceinline__ void lds_blocks(bf16x8_t (&f)[N], const uint8_t* base) {
   static_assert(N >= 1 && N <= 4, "blocks per step");
-  lds_fragment<0>(f[0], addr);
-  if constexpr (N > 1) lds_fragment<32 * kARowBytes>(f[N > 1 ? 1 : 0], addr);
-  if constexpr (N > 2) lds_fragment<64 * kARowBytes>(f[N > 2 ? 2 : 0], addr);
-  if constexpr (N > 3) lds_fragment<96 * kARowBytes>(f[N > 3 ? 3 : 0], addr);
-}
-
-// Waits for every fragment read issued so far and makes each fragment a
-// result of the wait, so nothing that uses one can be scheduled before it.
-template <int RB, int TN>
-__device__ __forceinline__ void lds_fragments_ready(bf16x8_t (&af)[RB], bf16x8_t (&bfr)[TN]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(af[rb]));
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(bfr[tn]));
+  for (int i = 0; i < N; ++i)
+    f[i] = *reinterpret_cast<const bf16x8_t*>(base + i * 32 * kARowBytes);
 }
 
 // Per-lane byte offsets of the 16-wide steps of a chunk inside an X tile
@@ -1154,12 +1136,11 @@ __device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int wcb)
 // step ks (scheduling barriers keep the compiler from merging the phases).
 template <int S, int TN, int RB>
 __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[RB][TN], const StageOffsets& o) {
-  const uint32_t xs = lds_address(stage_tile<S, false>());
-  const uint32_t ws = lds_address(stage_tile<S, true>());
+  const uint8_t* xs = stage_tile<S, false>();
+  const uint8_t* ws = stage_tile<S, true>();
   bf16x8_t af[2][RB], bfr[2][TN];
   lds_blocks<RB>(af[0], xs + o.x[0]);
   lds_blocks<TN>(bfr[0], ws + o.w[0]);
-  lds_fragments_ready<RB, TN>(af[0], bfr[0]);
 #pragma unroll
   for (int ks = 0; ks < kAKSteps; ++ks) {
     const int cur = ks & 1;
@@ -1175,7 +1156,6 @@ __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[RB][TN], const StageO
         acc[rb][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][rb], bfr[cur][tn],
                                                               acc[rb][tn], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < kAKSteps) lds_fragments_ready<RB, TN>(af[cur ^ 1], bfr[cur ^ 1]);
   }
 }
 
@@ -1221,19 +1201,6 @@ __device__ __forceinline__ void qp_fill(const float* qrow, int P, int lane) {
   __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)g_qp, 16, 0, 0);
 }
 
-// One float read from LDS byte address addr, untracked by the compiler like
-// lds_fragment(); ready after lds_values_ready().
-__device__ __forceinline__ void lds_value(float& v, uint32_t addr) {
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
-}
-
-template <int N>
-__device__ __forceinline__ void lds_values_ready(float (&v)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
-}
-
 // Epilogue of the ring kernel: as cos_epilogue, with q' taken from g_qp
 // (brought in by DMA when the question started, so nothing here waits on the
 // vector-memory counter) and barriers that do not wait for the next
@@ -1243,12 +1210,9 @@ template <int TN, int RB>
 __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
                                                   const f32x16_t (&acc)[RB][TN], int b, int K,
                                                   int lane, int wave, int wr, int wcb) {
-  const uint32_t qbase = lds_address(reinterpret_cast<const uint8_t*>(g_qp));
   float qv[TN];
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn)
-    lds_value(qv[tn], qbase + 4u * (uint32_t)(32 * TN * wcb + 32 * tn + (lane & 31)));
-  lds_values_ready<TN>(qv);
+  for (int tn = 0; tn < TN; ++tn) qv[tn] = g_qp[32 * TN * wcb + 32 * tn + (lane & 31)];
   // Accumulator e of tile (rb, tn) in lane l holds C'[row][col] with
   // row = 32*RB*wr + 32*rb + 8*(e/4) + 4*(l/32) + e%4 and
   // col = 32*TN*wcb + 32*tn + l%32; pairs of row blocks are reduced at once.
@@ -1295,8 +1259,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
   if (wave == 0) {
     float qpv[TN];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) lds_value(qpv[i], qbase + 4u * (uint32_t)(lane + kWave * i));
-    lds_values_ready<TN>(qpv);
+    for (int i = 0; i < TN; ++i) qpv[i] = g_qp[lane + kWave * i];
     float qq = 0.0f;
 #pragma unroll
     for (int i = 0; i < TN; ++i) qq = fmaf(qpv[i], qpv[i], qq);
@@ -1328,6 +1291,11 @@ __global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
   const int wr = wave % kRowGroups, wcb = wave / kRowGroups;
   const int H = a.D, K = a.K;
   const int nchunks = H / kAChunk;
+  // The host launches this kernel for H >= 64 only. Knowing that the chunk
+  // loop runs, the compiler sees every path to the epilogue pass a step's
+  // vmcnt(0) wait after the q' DMA, and lets the epilogue's reads of g_qp go
+  // ahead while the next question's first chunk is in flight.
+  __builtin_assume(nchunks >= 1);
   const bool carry = nchunks % kAStages == 0;
   const int stride = (int)gridDim.x;
   const StageOffsets o = stage_offsets<TN, RB>(lane, wr, wcb);
