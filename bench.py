@@ -14,9 +14,9 @@ Beside the headline it reports (same line):
     counters when the committed profile matches the current kernel source;
   * latency: single-question and small-batch calls timed through hipGraph
     replay (2000 replays of a one-node graph in five repetitions, the page's
-    protocol; median and min per call) next to an
-    empty kernel of the same grid and block replayed the same way: the launch
-    floor;
+    protocol; median and min per call) and as back-to-back direct calls,
+    each next to an empty kernel of the same grid and block timed the same
+    way: the launch floors of both protocols;
   * cpu_baseline: the double-precision oracle on the host, single-threaded
     (and, under "threaded", the same oracle over up to 16 host threads),
     over the same batch.
@@ -176,23 +176,90 @@ def latency_section(devc, replays):
             assert st == 0
             # five repetitions of replays/5 calls each; median (and min) per call
             n = max(1, replays // LATENCY_REPS)
-            g, d, f = [], [], []
+            g, d, f, fd = [], [], [], []
             nodes = 0
             for _ in range(LATENCY_REPS):
                 g_ms, nodes = devc.time_graph(call, n)
                 g.append(1e3 * g_ms / n)
                 d.append(1e3 * devc.time_calls(call, n) / n)
                 f.append(1e3 * devc.time_empty(grid, block, n, True) / n)
+                fd.append(1e3 * devc.time_empty(grid, block, n, False) / n)
+            direct, floor_direct = float(np.median(d)), float(np.median(fd))
             row[label] = {"groups": G, "grid": grid, "block": block,
                           "graph_us_per_call": round(float(np.median(g)), 3),
                           "graph_us_per_call_min": round(min(g), 3),
-                          "direct_us_per_call": round(float(np.median(d)), 3),
+                          "direct_us_per_call": round(direct, 3),
                           "direct_us_per_call_min": round(min(d), 3),
                           "graph_nodes": nodes,
                           "empty_kernel_graph_floor_us": round(float(np.median(f)), 3),
+                          "empty_kernel_direct_floor_us": round(floor_direct, 3),
+                          "empty_kernel_direct_floor_us_min": round(min(fd), 3),
+                          "direct_over_direct_floor": round(direct / floor_direct, 3),
                           "reps": LATENCY_REPS, "calls_per_rep": n}
         res[name] = row
         log(f"latency {name}: {row}")
+        del q, c, out
+    return res
+
+
+PHASES = [("loads and row sums", 0, 1), ("barrier", 1, 2), ("softmax and stores", 2, 3),
+          ("release fence", 3, 4), ("ticket", 4, 5)]
+LAST_PHASES = [("acquire fence", 6, 7), ("read e_k and partials, merge factors", 7, 8),
+               ("rescale, stores, reset", 8, 9)]
+PHASE_TICK_US = 0.01  # the device clock read by the stamps runs at 100 MHz
+
+
+def phase_clock_section(devc, calls=200, reps=40):
+    """Where a split call's time goes: the measurement build's per-phase
+    device clocks (thread 0 of each workgroup) for the last of `calls`
+    back-to-back direct calls, `reps` times; medians over repetitions of
+    the per-workgroup phase durations, of the merging (last) slice's phases
+    and of the kernel's span, beside the direct call rate and the empty
+    kernel's direct floor."""
+    cs, torch = devc.cs, devc.torch
+    lib = cs.load()
+    slots = 16
+    res = {}
+    for name in LATENCY_CONFIGS:
+        w = workloads.make(name)
+        q, c, out = devc.upload(w)
+        call, _ws = devc.call(w, q, c, out, use_workspace=True)
+        st, grid, block, G = cs.cs_plan_launch(w.B, w.K, w.D, w.similarity, True)
+        assert st == 0
+        if G < 2:
+            continue
+        devc.time_calls(call, 300)
+        direct = 1e3 * devc.time_calls(call, 2000) / 2000
+        floor = 1e3 * devc.time_empty(grid, block, 2000, False) / 2000
+        buf = np.zeros(grid * slots, dtype=np.uint64)
+        runs = []
+        for _ in range(reps):
+            devc.time_calls(call, calls)
+            torch.cuda.synchronize()
+            if lib.cs_phase_clocks_read(ctypes.c_void_p(buf.ctypes.data), buf.nbytes) != 0:
+                raise RuntimeError("cs_phase_clocks_read failed")
+            runs.append(buf.reshape(grid, slots).astype(np.int64))
+        T = np.stack(runs)                              # [rep, workgroup, slot]
+        if not np.all(T[:, :, 0] > 0):
+            raise RuntimeError("no phase clocks recorded: the calls did not reach libcs_phase.so")
+        t0 = T[:, :, 0].min(axis=1)
+        # the merging slice of the last call: slots 7..9 newer than its start
+        last = (T[:, :, 9] > T[:, :, 0]) & (T[:, :, 7] >= T[:, :, 0])
+        row = {"B": w.B, "K": w.K, "D": w.D, "similarity": w.similarity, "slices": G,
+               "workgroups": grid, "direct_us_per_call": round(direct, 3),
+               "empty_kernel_direct_floor_us": round(floor, 3)}
+        for label, a, b in PHASES:
+            row[label + " us"] = round(float(np.median((T[:, :, b] - T[:, :, a]) * PHASE_TICK_US)), 3)
+        for label, a, b in LAST_PHASES:
+            v = [float(((T[i][last[i]][:, b] - T[i][last[i]][:, a]) * PHASE_TICK_US).mean())
+                 for i in range(reps) if last[i].any()]
+            row["last slice: " + label + " us"] = round(float(np.median(v)), 3)
+        row["start spread us"] = round(float(np.median((T[:, :, 0].max(axis=1) - t0) * PHASE_TICK_US)), 3)
+        row["last ticket drawn at us"] = round(float(np.median((T[:, :, 5].max(axis=1) - t0) * PHASE_TICK_US)), 3)
+        row["kernel span us"] = round(float(np.median(
+            (np.maximum(T[:, :, 10].max(axis=1), T[:, :, 9].max(axis=1)) - t0) * PHASE_TICK_US)), 3)
+        res[name] = row
+        log(f"phase clocks {name}: {row}")
         del q, c, out
     return res
 
@@ -458,12 +525,31 @@ def main():
                     help="skip the projection + scoring workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
+    ap.add_argument("--phase-clocks", action="store_true",
+                    help="only the per-phase clocks of the split calls, from the measurement "
+                         "build candidate_scoring_amd/libcs_phase.so (python -m "
+                         "candidate_scoring_amd.build --phase-clocks)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(questions would shard across GPUs with no exchange, see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.phase_clocks:
+        import candidate_scoring_amd as cs_pkg
+
+        # First load in this process, and global: the native timing loop of
+        # libcs_bench.so then binds its calls to this build's entry points
+        # rather than to libcs.so, which it names as a dependency.
+        ctypes.CDLL(str(cs_pkg.PKG / "libcs_phase.so"), mode=ctypes.RTLD_GLOBAL)
+        lib = cs_pkg.load(cs_pkg.PKG / "libcs_phase.so")
+        lib.cs_phase_clocks_read.restype = ctypes.c_int
+        lib.cs_phase_clocks_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        devc = Device()
+        print(json.dumps({"phase_clocks": phase_clock_section(devc),
+                          "library": "libcs_phase.so (measurement build)"}), flush=True)
+        return
 
     devc = Device()
     torch = devc.torch

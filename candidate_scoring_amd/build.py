@@ -1,10 +1,12 @@
 """Builds the HIP libraries in-tree for gfx950 with hipcc.
 
-    python -m candidate_scoring_amd.build
+    python -m candidate_scoring_amd.build [--phase-clocks]
 
 produces ``candidate_scoring_amd/libcs.so`` (the C ABI of
 include/candidate_scoring.h) and ``candidate_scoring_amd/libcs_bench.so``
-(native timing helpers for bench.py).
+(native timing helpers for bench.py). With ``--phase-clocks`` it builds
+only ``libcs_phase.so``, a measurement copy of the library whose scoring
+kernels record per-phase device clocks (``bench.py --phase-clocks``).
 """
 from __future__ import annotations
 
@@ -109,6 +111,26 @@ def build(verbose: bool = False) -> list[Path]:
     return [LIBRARY, BENCH_LIBRARY]
 
 
+PHASE_LIBRARY = PKG / "libcs_phase.so"
+
+
+def build_phase_clocks(verbose: bool = False) -> Path:
+    """The measurement build: the same library with CS_PHASE_CLOCKS defined,
+    whose scoring kernels stamp the device clock at fixed phases (read with
+    cs_phase_clocks_read). Never loaded by the product path; built only on
+    request, for ``bench.py --phase-clocks``."""
+    cc = hipcc()
+    tmp = PHASE_LIBRARY.with_suffix(".so.tmp")
+    _run([cc, *common_flags(), "-DCS_PHASE_CLOCKS", "-o", str(tmp),
+          str(CSRC / "cs_kernels.hip"), str(CSRC / "cs_project.hip"), str(CSRC / "cs_api.cpp")],
+         verbose)
+    tmp.replace(PHASE_LIBRARY)
+    return PHASE_LIBRARY
+
+
 if __name__ == "__main__":
-    for p in build(verbose=True):
-        print("built", p)
+    if "--phase-clocks" in sys.argv[1:]:
+        print("built", build_phase_clocks(verbose=True))
+    else:
+        for p in build(verbose=True):
+            print("built", p)

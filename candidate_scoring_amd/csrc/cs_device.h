@@ -21,6 +21,30 @@
 namespace cs {
 namespace {
 
+// Phase clocks: a build with CS_PHASE_CLOCKS defined (libcs_phase.so, a
+// measurement build, never the product library) makes thread 0 of each
+// workgroup store the 100 MHz device clock at fixed points of the scoring
+// kernels and the split merge; in every other build CS_PHASE expands to
+// nothing. Slots: 0 start, 1 rows reduced (wave 0), 2 after the barrier,
+// 3 softmax stored, 4 release fence done, 5 ticket drawn, 6 after the
+// ticket barrier, 7 acquire done (last slice), 8 merge factors ready,
+// 9 rescaled and reset, 10 workgroup exit.
+#ifdef CS_PHASE_CLOCKS
+constexpr int kPhaseWorkgroups = 1024;
+constexpr int kPhaseSlots = 16;
+__device__ unsigned long long g_phase_clk[kPhaseWorkgroups * kPhaseSlots];
+#define CS_PHASE(slot)                                                                    \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)::cs::kPhaseWorkgroups)                \
+      ::cs::g_phase_clk[blockIdx.x * ::cs::kPhaseSlots + (slot)] =                          \
+          __builtin_amdgcn_s_memrealtime();                                               \
+  } while (0)
+#else
+#define CS_PHASE(slot) \
+  do {                 \
+  } while (0)
+#endif
+
 
 constexpr int kWave = 64;
 constexpr int kBlock = 512;        // threads per workgroup (upper bound)
@@ -339,16 +363,18 @@ __device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k
 
 // Softmax of this slice's n logits (wave 0 only) and the store of either the
 // final probabilities (one slice per question) or the unnormalised e_k plus
-// the slice's (max, sum) partial.
+// the slice's (max, sum) partial. VPL logits per lane (n <= 64 * VPL); the
+// slots past n hold -inf and exp 0, which leave the max and the sums
+// bitwise unchanged, so every VPL gives the same result.
 // MAYSPLIT = false: the caller never splits a question (a.G is 1).
-template <bool COS, bool MAYSPLIT = true>
-__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
-                                              int b, int g, int r0, int n, float zfac,
-                                              int lane) {
-  float z[4];
+template <bool COS, bool MAYSPLIT, int VPL>
+__device__ __forceinline__ void slice_softmax_vpl(const Lds& s, const KernelArgs& a,
+                                                  const Question& qn, int b, int g, int r0, int n,
+                                                  float zfac, int lane) {
+  float z[VPL];
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     const int k = lane + kWave * i;
     if (k < n) {
       float v = s.dot[k];
@@ -368,10 +394,10 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
     }
   }
   m = wave_allreduce(m, lane, OpMax());
-  float e[4];
+  float e[VPL];
   float l = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     const int k = lane + kWave * i;
     e[i] = (k < n) ? expf(z[i] - m) : 0.0f;
     l += e[i];
@@ -380,18 +406,31 @@ __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a,
   float* out = a.out + qn.row + r0;
   if (!MAYSPLIT || a.G == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int k = lane + kWave * i;
       if (k < n) out[k] = e[i] / l;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int k = lane + kWave * i;
       if (k < n) out[k] = e[i];
     }
     if (lane == 0) a.partials[(size_t)b * a.G + g] = make_float2(m, l);
   }
+}
+
+// A slice of at most 64 candidates (every slice of a split question, and
+// small questions) takes one logit per lane: a quarter of the LDS reads and
+// exponentials, on the critical path of every split call.
+template <bool COS, bool MAYSPLIT = true>
+__device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
+                                              int b, int g, int r0, int n, float zfac,
+                                              int lane) {
+  if (n <= kWave)
+    slice_softmax_vpl<COS, MAYSPLIT, 1>(s, a, qn, b, g, r0, n, zfac, lane);
+  else
+    slice_softmax_vpl<COS, MAYSPLIT, kMaxSlots / kWave>(s, a, qn, b, g, r0, n, zfac, lane);
 }
 
 // Called by every thread of a slice's workgroup after slice_softmax. With
@@ -403,17 +442,21 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
   // release fence orders the stores before the relaxed ticket increment.
   if (wave == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    CS_PHASE(4);
     if (lane == 0) {
       const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
       s.last = (t == (unsigned)(a.G - 1));
     }
+    CS_PHASE(5);
   }
   __syncthreads();
+  CS_PHASE(6);
   if (!s.last) return;  // uniform across the workgroup
   // Last slice: acquire the other slices' stores (L2 invalidate), fetch the
   // e_k to rescale while wave 0 reads the partials.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  CS_PHASE(7);
   float* out = a.out + qn.row;
   float ek[kMaxSlots / kWave];
 #pragma unroll
@@ -450,6 +493,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
     }
   }
   __syncthreads();
+  CS_PHASE(8);
 #pragma unroll
   for (int i = 0; i < kMaxSlots / kWave; ++i) {
     const int k = tid + (int)blockDim.x * i;
@@ -462,6 +506,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
   for (int g = tid; g < a.G; g += (int)blockDim.x)
     a.partials[(size_t)b * a.G + g] = make_float2(0.0f, 0.0f);
   if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  CS_PHASE(9);
 }
 
 }  // namespace

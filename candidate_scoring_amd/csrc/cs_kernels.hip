@@ -83,6 +83,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   // A ragged batch is never split: one item per question.
   const int G = RAGGED ? 1 : a.G;
   const long long items = (long long)a.B * G;
+  CS_PHASE(0);
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     int b = (int)(item / G);
     if constexpr (RAGGED) {
@@ -130,7 +131,9 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
       const float total = wave_reduce_transposed<V>(acc, lane, OpSum());
       store_group<COS, R>(s, total, lane, k0, r0, r1);
     }
+    CS_PHASE(1);
     __syncthreads();
+    CS_PHASE(2);
     if (wave == 0) {
       float zfac = a.zscale;
       if (COS || (a.cosine && a.staged_norms != nullptr)) {
@@ -141,10 +144,12 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
       }
       slice_softmax<COS, !RAGGED>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
+      CS_PHASE(3);
     }
     if (!RAGGED && a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
     __syncthreads();
   }
+  CS_PHASE(10);
 }
 
 // ---------------------------------------------------------------------------
@@ -443,3 +448,17 @@ hipError_t static_scratch(void** ptr, hipStream_t stream) {
 }
 
 }  // namespace cs
+
+#ifdef CS_PHASE_CLOCKS
+// Measurement build only: copies the phase clocks of the last launches
+// (workgroup-major, 16 slots each) to host memory, or clears them.
+extern "C" int cs_phase_clocks_read(void* dst, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(cs::g_phase_clk), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int cs_phase_clocks_clear(void) {
+  static unsigned long long zeros[cs::kPhaseWorkgroups * cs::kPhaseSlots];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(cs::g_phase_clk), zeros, sizeof(zeros), 0,
+                                hipMemcpyHostToDevice);
+}
+#endif
