@@ -338,7 +338,7 @@ def ragged_section(devc, iters=20):
 
     def once():
         st = cs.cs_score_candidates_ragged(q, c, o, B, rows, D, "dot", float(workloads.SCALE_DOT),
-                                           1.0, out, status, devc.stream)
+                                           1.0, out, status, stream=devc.stream)
         assert st == 0, st
 
     for _ in range(3):
@@ -357,6 +357,73 @@ def ragged_section(devc, iters=20):
            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     log(f"ragged: {res}")
     del q, c, o, out
+    res["small_batches"] = ragged_small_section(devc)
+    return res
+
+
+def ragged_small_section(devc, calls=2000):
+    """Small ragged batches spread over the chip (a zeroed workspace): 16
+    questions of 255 x 2560 (dot) next to the dense batch call on the same
+    data, and a batch of 8 questions with counts uniform in 1..255, each
+    also without a workspace (one workgroup per question). Back-to-back
+    direct calls, warm caches, median of five repetitions."""
+    torch, cs = devc.torch, devc.cs
+    res = {}
+    for label, B, counts_seed in (("16 x 255 rows", 16, None), ("8 questions, 1..255 rows", 8, 79)):
+        D = 2560
+        if counts_seed is None:
+            offsets = np.arange(B + 1, dtype=np.int64) * 255
+        else:
+            offsets = workloads.ragged_offsets(counts_seed, B)
+        Q, C = workloads.ragged_inputs(83, offsets, D)
+        rows = int(offsets[-1])
+        q, c = torch.from_numpy(Q).to(devc.dev), torch.from_numpy(C).to(devc.dev)
+        o = torch.from_numpy(offsets).to(devc.dev)
+        out = torch.empty(rows, dtype=torch.float32, device=devc.dev)
+        nbytes = cs.cs_ragged_workspace_bytes(B, rows, D, "dot")
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=devc.dev)
+        _, rpg, slices = cs.cs_plan_ragged(B, rows, D, "dot", True)
+
+        def timed(fn):
+            for _ in range(50):
+                fn()
+            t = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(devc.stream)
+                for _ in range(calls // 5):
+                    fn()
+                e1.record(devc.stream)
+                torch.cuda.synchronize()
+                t.append(1e3 * e0.elapsed_time(e1) / (calls // 5))
+            return round(float(np.median(t)), 3)
+
+        def ragged(w, n):
+            def f():
+                assert cs.cs_score_candidates_ragged(q, c, o, B, rows, D, "dot",
+                                                     float(workloads.SCALE_DOT), 1.0, out, None,
+                                                     w, n, devc.stream) == 0
+            return f
+
+        row = {"B": B, "rows": rows, "D": D, "rows_per_slice": rpg, "max_slices": slices,
+               "split_us_per_call": timed(ragged(ws, nbytes)),
+               "one_wg_per_question_us_per_call": timed(ragged(None, 0))}
+        if counts_seed is None:
+            dq, dc = q, c.reshape(B, 255, D)
+            dout = out.reshape(B, 255)
+            call, _dws = devc.call(workloads.Workload("dense", "batch", "dot",
+                                                      np.float32(workloads.SCALE_DOT),
+                                                      np.float32(1.0), Q, C.reshape(B, 255, D),
+                                                      ""), dq, dc, dout)
+            devc.time_calls(call, 50)
+            row["dense_batch_split_us_per_call"] = round(
+                float(np.median([1e3 * devc.time_calls(call, calls // 5) / (calls // 5)
+                                 for _ in range(5)])), 3)
+            row["ragged_over_dense"] = round(row["split_us_per_call"] /
+                                             row["dense_batch_split_us_per_call"], 3)
+        res[label] = row
+        log(f"ragged small {label}: {row}")
+        del q, c, o, out, ws
     return res
 
 

@@ -82,7 +82,10 @@ def load(path: Path | str = LIBRARY):
         "cs_score_projected": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp,
                                      vp, sz, vp]),
         "cs_score_candidates_ragged": (i32, [vp, vp, vp, i32, ctypes.c_int64, i32, i32, f32, f32,
-                                             vp, vp, vp]),
+                                             vp, vp, vp, sz, vp]),
+        "cs_ragged_workspace_bytes": (sz, [i32, ctypes.c_int64, i32, i32]),
+        "cs_plan_ragged": (i32, [i32, ctypes.c_int64, i32, i32, i32, ctypes.POINTER(ctypes.c_int),
+                                 ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -243,10 +246,23 @@ def cs_score_candidates_unfused(queries, candidates, B: int, K: int, D: int, sim
 
 def cs_score_candidates_ragged(queries, candidates, offsets, B: int, total_rows: int, D: int,
                                similarity, scale: float, temperature: float, out, status=None,
-                               stream=None) -> int:
+                               workspace=None, workspace_bytes: int = 0, stream=None) -> int:
     return load().cs_score_candidates_ragged(_ptr(queries), _ptr(candidates), _ptr(offsets), B,
                                              total_rows, D, _sim(similarity), scale, temperature,
-                                             _ptr(out), _ptr(status), _stream(stream))
+                                             _ptr(out), _ptr(status), _ptr(workspace),
+                                             workspace_bytes, _stream(stream))
+
+
+def cs_ragged_workspace_bytes(B: int, total_rows: int, D: int, similarity) -> int:
+    return load().cs_ragged_workspace_bytes(B, total_rows, D, _sim(similarity))
+
+
+def cs_plan_ragged(B: int, total_rows: int, D: int, similarity, has_workspace: bool):
+    """(status, rows_per_slice, max_slices) of the ragged call's plan."""
+    rpg, slices = ctypes.c_int(), ctypes.c_int()
+    st = load().cs_plan_ragged(B, total_rows, D, _sim(similarity), int(bool(has_workspace)),
+                               ctypes.byref(rpg), ctypes.byref(slices))
+    return st, rpg.value, slices.value
 
 
 def cs_projected_workspace_bytes(B: int, Hc: int, P: int, similarity) -> int:
@@ -326,12 +342,15 @@ def score(query, candidates, similarity="cosine", scale=1.0, temperature=1.0, ou
 
 
 def score_ragged(queries, candidates, offsets, similarity="cosine", scale=1.0,
-                 temperature=1.0, out=None, status=None, stream=None):
+                 temperature=1.0, out=None, status=None, use_workspace=True, stream=None):
     """Probabilities for a ragged batch: queries [B, D], candidates
     [total_rows, D] packed by question, offsets int64 [B + 1] on the device
     (question b owns rows offsets[b] .. offsets[b+1]-1, 1 to 255 of them).
     Returns out [total_rows]. A question with bad offsets is skipped and, if
-    ``status`` (an int32 device tensor) is given, flagged there."""
+    ``status`` (an int32 device tensor) is given, flagged there. A small
+    batch spreads its questions over the chip through the cached zeroed
+    workspace that score() uses (use_workspace=False: one workgroup per
+    question)."""
     import torch
 
     B, D = queries.shape
@@ -345,8 +364,14 @@ def score_ragged(queries, candidates, offsets, similarity="cosine", scale=1.0,
     for t in (queries, candidates, out):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("fp32 contiguous tensors required")
+    ws, nbytes = None, 0
+    if use_workspace:
+        nbytes = cs_ragged_workspace_bytes(B, total_rows, D, similarity)
+        if nbytes > 0:
+            ws = workspace(nbytes, candidates.device, stream)
+            nbytes = ws.numel()
     st = cs_score_candidates_ragged(queries, candidates, offsets, B, total_rows, D, similarity,
-                                    scale, temperature, out, status, stream)
+                                    scale, temperature, out, status, ws, nbytes, stream)
     if st != CS_OK:
         raise ScoringError(st)
     return out

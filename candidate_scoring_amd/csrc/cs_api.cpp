@@ -63,8 +63,8 @@ constexpr double kMinUsefulSlices = 3.5;
 constexpr double kLargeQuestionBytes = 1.0e6;
 constexpr double kMinUsefulSlicesLarge = 2.5;
 constexpr int kMaxSlices = 64;
-// Compute units of MI355X: the most slice workgroups a batch is given.
-constexpr int kMaxSliceWorkgroups = 256;
+// Compute units assumed when the device cannot be queried (MI355X has 256).
+constexpr int kDefaultComputeUnits = 256;
 // Grid cap; items beyond it are strided over the resident workgroups.
 constexpr long long kGridCap = 1 << 20;
 
@@ -133,9 +133,17 @@ int device_compute_units() {
   return n;
 }
 
+// Compute units to plan for: the current device's, or MI355X's 256 when
+// there is no device to ask (host-only planning queries).
+int planning_compute_units() {
+  const int n = device_compute_units();
+  return n > 0 ? n : kDefaultComputeUnits;
+}
+
 // Slices per question for a candidate pass that streams bytes_q per question
-// with waves of R rows each (the shared core of both planners).
-int plan_slices(int B, int K, double bytes_q, int R) {
+// with waves of R rows each, on a device of `cus` compute units (the shared
+// core of both planners; a pure function of its arguments).
+int plan_slices(int B, int K, double bytes_q, int R, int cus) {
   if (K == 1) return 1;
   if (bytes_q < kMinSplitBytes) return 1;
   const double g_star = std::sqrt(bytes_q / ((double)B * kSliceBalanceBytes));
@@ -156,7 +164,7 @@ int plan_slices(int B, int K, double bytes_q, int R) {
   }
   // At most one slice workgroup per compute unit: past that, two slices
   // share a unit and the batch took 30-50 % longer.
-  G = std::min(G, std::max(1, kMaxSliceWorkgroups / B));
+  G = std::min(G, std::max(1, cus / B));
   if (G < 2) return 1;
   rpg = (K + G - 1) / G;
   return (K + rpg - 1) / rpg;  // no empty slices
@@ -164,9 +172,34 @@ int plan_slices(int B, int K, double bytes_q, int R) {
 
 // fp32 scoring: R of the kernel variant D selects (the general kernel's 4
 // when no register-query variant covers D).
-int plan_groups(int B, int K, int D) {
+int plan_groups(int B, int K, int D, int cus) {
   const int nv = D % 4 == 0 ? cs::regq_nv_for(D) : 0;
-  return plan_slices(B, K, 4.0 * (double)K * (double)D, nv > 0 ? cs::regq_rows_per_wave(nv) : 4);
+  return plan_slices(B, K, 4.0 * (double)K * (double)D, nv > 0 ? cs::regq_rows_per_wave(nv) : 4,
+                     cus);
+}
+
+// Ragged batches are planned from their mean count: rows per slice as the
+// dense planner would cut a question of that many rows, so a question of K_b
+// rows takes ceil(K_b / rpg) slices and every slice carries about the same
+// work. rpg is at least ceil(255 * B / cus), so even a batch of 255-row
+// questions launches no more slice workgroups than compute units, and at
+// least ceil(255 / 64), the dense planner's slice limit. max_slices 1: every
+// question in one workgroup.
+struct RaggedPlan {
+  int rpg;
+  int max_slices;
+};
+
+RaggedPlan plan_ragged(int B, long long total_rows, int D, int cus) {
+  const long long mean = std::min<long long>(CS_MAX_K, std::max<long long>(1, total_rows / B));
+  const int G = plan_groups(B, (int)mean, D, cus);
+  if (G < 2) return {CS_MAX_K, 1};
+  int rpg = (int)((mean + G - 1) / G);
+  rpg = std::max({rpg, (int)((CS_MAX_K * (long long)B + cus - 1) / cus),
+                  (CS_MAX_K + kMaxSlices - 1) / kMaxSlices});
+  const int max_slices = (CS_MAX_K + rpg - 1) / rpg;
+  if (max_slices < 2) return {CS_MAX_K, 1};
+  return {rpg, max_slices};
 }
 
 // Launch shape for a validated call: kernel variant from D and alignment,
@@ -273,15 +306,24 @@ int score_unfused(const float* Q, const float* C, int B, int K, int D, int sim, 
 // out; one workgroup per question, which checks its own offsets.
 int score_ragged(const float* Q, const float* C, const long long* offsets, int B,
                  long long total_rows, int D, int sim, float scale, float temperature, float* out,
-                 int* status, hipStream_t stream) {
+                 int* status, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (offsets == nullptr) return CS_ERR_NULL_POINTER;
   int st = validate(Q, C, out, B, 1, D, sim, scale, temperature);
   if (st != CS_OK) return st;
   // every question needs 1..255 rows
   if (total_rows < (long long)B || total_rows > (long long)B * CS_MAX_K) return CS_ERR_K_RANGE;
+  // A workspace spreads the questions of a small batch over several
+  // workgroups each; without one (or for a large batch) one per question.
+  const RaggedPlan plan = ws != nullptr ? plan_ragged(B, total_rows, D, planning_compute_units())
+                                        : RaggedPlan{CS_MAX_K, 1};
+  const bool split = plan.max_slices > 1;
+  if (split && (ws_bytes < workspace_for(B, plan.max_slices) ||
+                (reinterpret_cast<uintptr_t>(ws) & 7u) != 0))
+    return CS_ERR_WORKSPACE;
   if (debug_pointers()) {
     if (!is_device_pointer(Q) || !is_device_pointer(C) || !is_device_pointer(out) ||
-        !is_device_pointer(offsets) || (status != nullptr && !is_device_pointer(status)))
+        !is_device_pointer(offsets) || (status != nullptr && !is_device_pointer(status)) ||
+        (split && !is_device_pointer(ws)))
       return CS_ERR_HOST_POINTER;
   }
   cs::KernelArgs a{};
@@ -291,8 +333,11 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   a.B = B;
   a.K = CS_MAX_K;  // upper bound; each question's own count comes from offsets
   a.D = D;
-  a.G = 1;
-  a.rpg = CS_MAX_K;
+  a.G = plan.max_slices;
+  a.rpg = plan.rpg;
+  a.tickets = split ? static_cast<unsigned*>(ws) : nullptr;
+  a.partials = split ? reinterpret_cast<float2*>(static_cast<char*>(ws) + ticket_bytes(B))
+                     : nullptr;
   a.zscale = (float)((double)scale / (double)temperature);
   a.cosine = sim == CS_SIM_COSINE;
   a.offsets = offsets;
@@ -303,11 +348,13 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   // that order costs every workgroup one pass over the B+1 offsets, so it is
   // used only while that pass is small next to a question's own rows.
   const double mean_question_bytes = 4.0 * (double)total_rows / (double)B * (double)D;
-  a.longest_first =
-      (B > kResidentQuestions && 8.0 * (double)B * kRankCostRatio <= mean_question_bytes) ? 1 : 0;
+  a.longest_first = (!split && B > kResidentQuestions &&
+                     8.0 * (double)B * kRankCostRatio <= mean_question_bytes)
+                        ? 1
+                        : 0;
   // launch shape as for a dense batch of the same total size
-  const int mean_k = (int)std::max<long long>(1, total_rows / B);
-  cs::LaunchShape ls = make_shape(B, mean_k, D, 1, CS_MAX_K, Q, C);
+  const int mean_k = (int)std::max<long long>(1, std::min<long long>(CS_MAX_K, total_rows / B));
+  cs::LaunchShape ls = make_shape(B, mean_k, D, plan.max_slices, plan.rpg, Q, C);
   ls.nt = 4.0 * (double)total_rows * (double)D >= kStreamBytes ? 1 : 0;
   const hipError_t err = cs::launch_fused(a, ls, stream);
   if (err != hipSuccess) {
@@ -401,7 +448,7 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.cos_slice =
       sim == CS_SIM_COSINE && slice_groups <= (cos_slices == 1 ? cus : cus / 4) ? 1 : 0;
   p.G = sim == CS_SIM_DOT ? plan_slices(B, K, 2.0 * (double)K * (double)Hc,
-                                        cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)))
+                                        cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)), cus)
                           : (p.cos_slice ? cos_slices : 1);
   p.B = B;
   p.K = K;
@@ -449,7 +496,7 @@ int cs_last_hip_error(void) { return g_last_hip_error; }
 
 int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace) {
   if (validate(&B, &B, &B, B, K, D, similarity, 1.0f, 1.0f) != CS_OK) return 0;
-  return has_workspace ? plan_groups(B, K, D) : 1;
+  return has_workspace ? plan_groups(B, K, D, planning_compute_units()) : 1;
 }
 
 int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
@@ -499,7 +546,7 @@ int cs_score_candidates_batch(const float* queries, const float* candidates, int
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = validate(queries, candidates, out, B, K, D, similarity, scale, temperature);
   if (st != CS_OK) return st;
-  const int G = workspace != nullptr ? plan_groups(B, K, D) : 1;
+  const int G = workspace != nullptr ? plan_groups(B, K, D, planning_compute_units()) : 1;
   return score(queries, candidates, B, K, D, similarity, scale, temperature, out, workspace,
                workspace_bytes, G, stream);
 }
@@ -510,7 +557,7 @@ int cs_score_candidates_batch_noalloc(const float* queries, const float* candida
   int st = validate(queries, candidates, out, B, K, D, similarity, scale, temperature);
   if (st != CS_OK) return st;
   static_assert(cs::kStaticScratchBytes == CS_NOALLOC_SCRATCH_BYTES, "one scratch size");
-  const int G = plan_groups(B, K, D);
+  const int G = plan_groups(B, K, D, planning_compute_units());
   if (G <= 1)  // one workgroup per question: no workspace at all
     return score(queries, candidates, B, K, D, similarity, scale, temperature, out, nullptr, 0,
                  1, stream);
@@ -536,11 +583,31 @@ int cs_score_candidates_unfused(const float* queries, const float* candidates, i
 int cs_score_candidates_ragged(const float* queries, const float* candidates,
                                const int64_t* offsets, int B, int64_t total_rows, int D,
                                int similarity, float scale, float temperature, float* out,
-                               int* status, hipStream_t stream) {
+                               int* status, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   static_assert(sizeof(int64_t) == sizeof(long long), "offsets are 64-bit");
   return score_ragged(queries, candidates, reinterpret_cast<const long long*>(offsets), B,
                       (long long)total_rows, D, similarity, scale, temperature, out, status,
-                      stream);
+                      workspace, workspace_bytes, stream);
+}
+
+int cs_plan_ragged(int B, int64_t total_rows, int D, int similarity, int has_workspace,
+                   int* rows_per_slice, int* max_slices) {
+  int st = validate(&B, &B, &B, B, 1, D, similarity, 1.0f, 1.0f);
+  if (st != CS_OK) return st;
+  if (total_rows < (int64_t)B || total_rows > (int64_t)B * CS_MAX_K) return CS_ERR_K_RANGE;
+  const RaggedPlan plan = has_workspace
+                              ? plan_ragged(B, (long long)total_rows, D, planning_compute_units())
+                              : RaggedPlan{CS_MAX_K, 1};
+  if (rows_per_slice) *rows_per_slice = plan.rpg;
+  if (max_slices) *max_slices = plan.max_slices;
+  return CS_OK;
+}
+
+size_t cs_ragged_workspace_bytes(int B, int64_t total_rows, int D, int similarity) {
+  int rpg = 0, slices = 0;
+  if (cs_plan_ragged(B, total_rows, D, similarity, 1, &rpg, &slices) != CS_OK) return 0;
+  return workspace_for(B, slices);
 }
 
 size_t cs_projected_workspace_bytes(int B, int Hc, int P, int similarity) {

@@ -54,6 +54,18 @@ constexpr int kStatusBadOffsets = -2;  // the K-range status of the C ABI
 constexpr float kNormEps = 1e-12f;   // per-norm clamp of the cosine
 constexpr float kNormEps2 = 1e-24f;  // its square, for clamping squared norms
 
+// How a scoring launch maps work items to questions.
+//  kDense: B questions of K rows each, every question in a.G slices of
+//    a.rpg rows (one slice: the whole question).
+//  kRagged: question b owns rows offsets[b] .. offsets[b+1]-1 (read on the
+//    device); one work item per question, never split.
+//  kRaggedSplit: ragged, with every question cut into slices of a.rpg rows;
+//    a.G is the most slices any question can have (255 rows), and question b
+//    uses ceil(K_b / a.rpg) of them, merged like a split dense question.
+constexpr int kDense = 0;
+constexpr int kRagged = 1;
+constexpr int kRaggedSplit = 2;
+
 // ---------------------------------------------------------------------------
 // Cross-lane primitives (wave64).
 
@@ -362,15 +374,16 @@ __device__ __forceinline__ void store_group(Lds& s, float total, int lane, int k
 }
 
 // Softmax of this slice's n logits (wave 0 only) and the store of either the
-// final probabilities (one slice per question) or the unnormalised e_k plus
-// the slice's (max, sum) partial. VPL logits per lane (n <= 64 * VPL); the
+// final probabilities (the question has one slice) or the unnormalised e_k
+// plus the slice's (max, sum) partial (partial g of question b at
+// b * a.G + g; the question has nslices <= a.G slices). VPL logits per lane (n <= 64 * VPL); the
 // slots past n hold -inf and exp 0, which leave the max and the sums
 // bitwise unchanged, so every VPL gives the same result.
-// MAYSPLIT = false: the caller never splits a question (a.G is 1).
+// MAYSPLIT = false: the caller never splits a question (nslices is 1).
 template <bool COS, bool MAYSPLIT, int VPL>
 __device__ __forceinline__ void slice_softmax_vpl(const Lds& s, const KernelArgs& a,
                                                   const Question& qn, int b, int g, int r0, int n,
-                                                  float zfac, int lane) {
+                                                  float zfac, int lane, int nslices) {
   float z[VPL];
   float m = -INFINITY;
 #pragma unroll
@@ -404,7 +417,7 @@ __device__ __forceinline__ void slice_softmax_vpl(const Lds& s, const KernelArgs
   }
   l = wave_allreduce(l, lane, OpSum());
   float* out = a.out + qn.row + r0;
-  if (!MAYSPLIT || a.G == 1) {
+  if (!MAYSPLIT || nslices == 1) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int k = lane + kWave * i;
@@ -425,18 +438,20 @@ __device__ __forceinline__ void slice_softmax_vpl(const Lds& s, const KernelArgs
 // exponentials, on the critical path of every split call.
 template <bool COS, bool MAYSPLIT = true>
 __device__ __forceinline__ void slice_softmax(const Lds& s, const KernelArgs& a, const Question& qn,
-                                              int b, int g, int r0, int n, float zfac,
-                                              int lane) {
+                                              int b, int g, int r0, int n, float zfac, int lane,
+                                              int nslices) {
   if (n <= kWave)
-    slice_softmax_vpl<COS, MAYSPLIT, 1>(s, a, qn, b, g, r0, n, zfac, lane);
+    slice_softmax_vpl<COS, MAYSPLIT, 1>(s, a, qn, b, g, r0, n, zfac, lane, nslices);
   else
-    slice_softmax_vpl<COS, MAYSPLIT, kMaxSlots / kWave>(s, a, qn, b, g, r0, n, zfac, lane);
+    slice_softmax_vpl<COS, MAYSPLIT, kMaxSlots / kWave>(s, a, qn, b, g, r0, n, zfac, lane,
+                                                         nslices);
 }
 
-// Called by every thread of a slice's workgroup after slice_softmax. With
-// several slices per question, the last slice to arrive merges.
+// Called by every thread of a slice's workgroup after slice_softmax, when
+// question b has nslices > 1 slices of a.rpg rows (its partials start at
+// b * a.G): the last slice to arrive merges.
 __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Question& qn,
-                                            int b, int tid, int lane, int wave) {
+                                            int b, int tid, int lane, int wave, int nslices) {
   // Only wave 0 wrote global memory (e_k and the partial). It publishes them
   // at agent scope (all XCDs: L2 write-back) and draws the ticket; the
   // release fence orders the stores before the relaxed ticket increment.
@@ -446,7 +461,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
     if (lane == 0) {
       const unsigned t = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-      s.last = (t == (unsigned)(a.G - 1));
+      s.last = (t == (unsigned)(nslices - 1));
     }
     CS_PHASE(5);
   }
@@ -471,7 +486,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = lane + kWave * i;
-      const float2 v = (g < a.G) ? part[g] : make_float2(-INFINITY, 0.0f);
+      const float2 v = (g < nslices) ? part[g] : make_float2(-INFINITY, 0.0f);
       mg[i] = v.x;
       lg[i] = v.y;
       M = fmaxf(M, mg[i]);
@@ -482,14 +497,14 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = lane + kWave * i;
-      w[i] = (g < a.G) ? expf(mg[i] - M) : 0.0f;
+      w[i] = (g < nslices) ? expf(mg[i] - M) : 0.0f;
       L += lg[i] * w[i];
     }
     L = wave_allreduce(L, lane, OpSum());
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = lane + kWave * i;
-      if (g < a.G) s.merge[g] = w[i] / L;
+      if (g < nslices) s.merge[g] = w[i] / L;
     }
   }
   __syncthreads();
@@ -503,7 +518,7 @@ __device__ __forceinline__ void split_merge(Lds& s, const KernelArgs& a, const Q
   // (read above, before the barrier) and its ticket. The ticket array's
   // length depends on B, so a later call with more questions finds its
   // tickets where this call kept partials; those must read as zero.
-  for (int g = tid; g < a.G; g += (int)blockDim.x)
+  for (int g = tid; g < nslices; g += (int)blockDim.x)
     a.partials[(size_t)b * a.G + g] = make_float2(0.0f, 0.0f);
   if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   CS_PHASE(9);

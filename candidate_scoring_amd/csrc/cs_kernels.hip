@@ -74,26 +74,30 @@ namespace {
 // hot loop; the query's squared norm is reduced once per workgroup (by wave
 // 0, which holds all of q) right before the softmax.
 
-template <bool COS, int NV, int R, bool FULL, bool NT, bool RAGGED>
+template <bool COS, int NV, int R, bool FULL, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int D4 = a.D >> 2;
-  // A ragged batch is never split: one item per question.
-  const int G = RAGGED ? 1 : a.G;
+  // Work items per question: one for an unsplit ragged batch.
+  const int G = MODE == kRagged ? 1 : a.G;
   const long long items = (long long)a.B * G;
   CS_PHASE(0);
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     int b = (int)(item / G);
-    if constexpr (RAGGED) {
+    if constexpr (MODE == kRagged) {
       if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
     }
     const int g = (int)(item % G);
     Question qn;
-    if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
-    const int r0 = RAGGED ? 0 : g * a.rpg;
-    const int r1 = RAGGED ? qn.K : min(qn.K, r0 + a.rpg);
+    if (!resolve_question<MODE != kDense>(a, b, tid, qn)) continue;  // uniform per workgroup
+    const int r0 = MODE == kRagged ? 0 : g * a.rpg;
+    // A ragged question has only ceil(K_b / rpg) of the a.G slices.
+    if (MODE == kRaggedSplit && r0 >= qn.K) continue;  // uniform per workgroup
+    const int r1 = MODE == kRagged ? qn.K : min(qn.K, r0 + a.rpg);
+    const int nslices =
+        MODE == kDense ? a.G : MODE == kRagged ? 1 : (qn.K + a.rpg - 1) / a.rpg;
     const float4* q4 = reinterpret_cast<const float4*>(a.Q + (size_t)b * (size_t)a.D);
     float4 qr[NV];
 #pragma unroll
@@ -143,10 +147,10 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         qq = wave_allreduce(qq, lane, OpSum());
         zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
       }
-      slice_softmax<COS, !RAGGED>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
+      slice_softmax<COS, MODE != kRagged>(s, a, qn, b, g, r0, r1 - r0, zfac, lane, nslices);
       CS_PHASE(3);
     }
-    if (!RAGGED && a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+    if (MODE != kRagged && nslices > 1) split_merge(s, a, qn, b, tid, lane, wave, nslices);
     __syncthreads();
   }
   CS_PHASE(10);
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
 
 constexpr int kQChunk = 8192;
 
-template <bool COS, int VEC, bool NT, bool RAGGED>
+template <bool COS, int VEC, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   extern __shared__ float q_dyn[];
   __shared__ Lds s;
@@ -169,19 +173,23 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
   constexpr int V = COS ? 2 * R : R;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
-  // A ragged batch is never split: one item per question.
-  const int G = RAGGED ? 1 : a.G;
+  // Work items per question: one for an unsplit ragged batch.
+  const int G = MODE == kRagged ? 1 : a.G;
   const long long items = (long long)a.B * G;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     int b = (int)(item / G);
-    if constexpr (RAGGED) {
+    if constexpr (MODE == kRagged) {
       if (a.longest_first) b = question_of_rank(a, (int)item, s, tid, lane, wave);
     }
     const int g = (int)(item % G);
     Question qn;
-    if (!resolve_question<RAGGED>(a, b, tid, qn)) continue;  // uniform per workgroup
-    const int r0 = RAGGED ? 0 : g * a.rpg;
-    const int r1 = RAGGED ? qn.K : min(qn.K, r0 + a.rpg);
+    if (!resolve_question<MODE != kDense>(a, b, tid, qn)) continue;  // uniform per workgroup
+    const int r0 = MODE == kRagged ? 0 : g * a.rpg;
+    // A ragged question has only ceil(K_b / rpg) of the a.G slices.
+    if (MODE == kRaggedSplit && r0 >= qn.K) continue;  // uniform per workgroup
+    const int r1 = MODE == kRagged ? qn.K : min(qn.K, r0 + a.rpg);
+    const int nslices =
+        MODE == kDense ? a.G : MODE == kRagged ? 1 : (qn.K + a.rpg - 1) / a.rpg;
     const float* qb = a.Q + (size_t)b * (size_t)a.D;
     const float* Cb = a.C + qn.row * (size_t)a.D;
     const bool need_qq = COS || (a.cosine && a.staged_norms != nullptr);
@@ -249,8 +257,9 @@ __global__ __launch_bounds__(kBlock) void fused_general(KernelArgs a) {
     } else {
       __syncthreads();
     }
-    if (wave == 0) slice_softmax<COS, !RAGGED>(s, a, qn, b, g, r0, r1 - r0, zfac, lane);
-    if (!RAGGED && a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+    if (wave == 0)
+      slice_softmax<COS, MODE != kRagged>(s, a, qn, b, g, r0, r1 - r0, zfac, lane, nslices);
+    if (MODE != kRagged && nslices > 1) split_merge(s, a, qn, b, tid, lane, wave, nslices);
     __syncthreads();
   }
 }
@@ -307,52 +316,52 @@ __global__ void zero_bytes(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Launch selection.
 
-template <bool COS, int NV, int R, bool NT, bool RAGGED>
+template <bool COS, int NV, int R, bool NT, int MODE>
 hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const bool full = (a.D >> 2) == NV * kWave;
   if (full)
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT, RAGGED>), dim3(ls.grid), dim3(ls.block),
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT, MODE>), dim3(ls.grid), dim3(ls.block),
                        0, stream, a);
   else
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT, RAGGED>), dim3(ls.grid),
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT, MODE>), dim3(ls.grid),
                        dim3(ls.block), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool COS, bool NT, bool RAGGED>
+template <bool COS, bool NT, int MODE>
 hipError_t launch_regq(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   switch (ls.nv) {
-    case 1: return launch_regq_nv<COS, 1, 8, NT, RAGGED>(a, ls, stream);
-    case 2: return launch_regq_nv<COS, 2, 8, NT, RAGGED>(a, ls, stream);
-    case 4: return launch_regq_nv<COS, 4, 4, NT, RAGGED>(a, ls, stream);
-    case 6: return launch_regq_nv<COS, 6, 2, NT, RAGGED>(a, ls, stream);
-    case 8: return launch_regq_nv<COS, 8, 2, NT, RAGGED>(a, ls, stream);
-    case 10: return launch_regq_nv<COS, 10, 2, NT, RAGGED>(a, ls, stream);
-    case 12: return launch_regq_nv<COS, 12, 1, NT, RAGGED>(a, ls, stream);
-    case 16: return launch_regq_nv<COS, 16, 1, NT, RAGGED>(a, ls, stream);
+    case 1: return launch_regq_nv<COS, 1, 8, NT, MODE>(a, ls, stream);
+    case 2: return launch_regq_nv<COS, 2, 8, NT, MODE>(a, ls, stream);
+    case 4: return launch_regq_nv<COS, 4, 4, NT, MODE>(a, ls, stream);
+    case 6: return launch_regq_nv<COS, 6, 2, NT, MODE>(a, ls, stream);
+    case 8: return launch_regq_nv<COS, 8, 2, NT, MODE>(a, ls, stream);
+    case 10: return launch_regq_nv<COS, 10, 2, NT, MODE>(a, ls, stream);
+    case 12: return launch_regq_nv<COS, 12, 1, NT, MODE>(a, ls, stream);
+    case 16: return launch_regq_nv<COS, 16, 1, NT, MODE>(a, ls, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool COS, bool NT, bool RAGGED>
+template <bool COS, bool NT, int MODE>
 hipError_t launch_general(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const size_t lds = sizeof(float) * (size_t)min(a.D, kQChunk);
   if (ls.vec == 4)
-    hipLaunchKernelGGL((fused_general<COS, 4, NT, RAGGED>), dim3(ls.grid), dim3(ls.block), lds,
+    hipLaunchKernelGGL((fused_general<COS, 4, NT, MODE>), dim3(ls.grid), dim3(ls.block), lds,
                        stream, a);
   else
-    hipLaunchKernelGGL((fused_general<COS, 1, NT, RAGGED>), dim3(ls.grid), dim3(ls.block), lds,
+    hipLaunchKernelGGL((fused_general<COS, 1, NT, MODE>), dim3(ls.grid), dim3(ls.block), lds,
                        stream, a);
   return hipGetLastError();
 }
 
-template <bool COS, bool RAGGED>
+template <bool COS, int MODE>
 hipError_t launch_kind(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   if (ls.nv > 0)
-    return ls.nt ? launch_regq<COS, true, RAGGED>(a, ls, stream)
-                 : launch_regq<COS, false, RAGGED>(a, ls, stream);
-  return ls.nt ? launch_general<COS, true, RAGGED>(a, ls, stream)
-               : launch_general<COS, false, RAGGED>(a, ls, stream);
+    return ls.nt ? launch_regq<COS, true, MODE>(a, ls, stream)
+                 : launch_regq<COS, false, MODE>(a, ls, stream);
+  return ls.nt ? launch_general<COS, true, MODE>(a, ls, stream)
+               : launch_general<COS, false, MODE>(a, ls, stream);
 }
 
 }  // namespace
@@ -378,11 +387,14 @@ int regq_nv_for(int D) {
 hipError_t launch_fused(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   // With staged norms (unfused baseline) the hot loop accumulates dots only.
   const bool accumulate_norms = a.cosine && a.staged_norms == nullptr;
+  if (a.offsets != nullptr && a.G > 1)
+    return accumulate_norms ? launch_kind<true, kRaggedSplit>(a, ls, stream)
+                            : launch_kind<false, kRaggedSplit>(a, ls, stream);
   if (a.offsets != nullptr)
-    return accumulate_norms ? launch_kind<true, true>(a, ls, stream)
-                            : launch_kind<false, true>(a, ls, stream);
-  return accumulate_norms ? launch_kind<true, false>(a, ls, stream)
-                          : launch_kind<false, false>(a, ls, stream);
+    return accumulate_norms ? launch_kind<true, kRagged>(a, ls, stream)
+                            : launch_kind<false, kRagged>(a, ls, stream);
+  return accumulate_norms ? launch_kind<true, kDense>(a, ls, stream)
+                          : launch_kind<false, kDense>(a, ls, stream);
 }
 
 hipError_t launch_row_norms(const float* C, long long rows, int D, int vec, int nt, float* norms,

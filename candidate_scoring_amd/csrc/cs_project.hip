@@ -709,8 +709,8 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
       store_group<false, R>(s, total, lane, k0, r0, r1);
     }
     __syncthreads();
-    if (wave == 0) slice_softmax<false>(s, a, qn, b, g, r0, r1 - r0, a.zscale, lane);
-    if (G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+    if (wave == 0) slice_softmax<false>(s, a, qn, b, g, r0, r1 - r0, a.zscale, lane, G);
+    if (G > 1) split_merge(s, a, qn, b, tid, lane, wave, G);
     __syncthreads();
   }
 }
@@ -770,7 +770,7 @@ __device__ __forceinline__ void cos_epilogue(Lds& s, const KernelArgs& a,
     qq = wave_allreduce(qq, lane, OpSum());
     const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
     const Question qn{(size_t)b * (size_t)K, K};
-    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane);
+    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane, a.G);
   }
   __syncthreads();
 }
@@ -1008,9 +1008,9 @@ __global__ __launch_bounds__(kCosSliceWaves * kWave) void proj_cos_slice(
     for (int i = 0; i < 4; ++i) qq = fmaf(qs[lane + kWave * i], qs[lane + kWave * i], qq);
     qq = wave_allreduce(qq, lane, OpSum());
     const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
-    slice_softmax<true>(s, a, qn, b, g, r0, n, zfac, lane);
+    slice_softmax<true>(s, a, qn, b, g, r0, n, zfac, lane, a.G);
   }
-  if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave);
+  if (a.G > 1) split_merge(s, a, qn, b, tid, lane, wave, a.G);
 }
 
 // ---------------------------------------------------------------------------
@@ -1266,7 +1266,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
     qq = wave_allreduce(qq, lane, OpSum());
     const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
     const Question qn{(size_t)b * (size_t)K, K};
-    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane);
+    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane, a.G);
   }
   // No barrier here: wave 0 reaches the next question's first ring barrier
   // only after the softmax, and s.dot / s.ss are written again only after it.

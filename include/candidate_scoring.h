@@ -158,25 +158,47 @@ int cs_score_candidates_batch_noalloc(const float *queries, const float *candida
                                       int K, int D, int similarity, float scale,
                                       float temperature, float *out, hipStream_t stream);
 
-/* Ragged batch: B questions with their own candidate counts, one launch.
- * Question b owns candidate rows offsets[b] .. offsets[b+1]-1 of
- * candidates [total_rows][D] and the same slots of out [total_rows];
- * queries is [B][D]. offsets is a DEVICE array of B+1 int64 values with
- * offsets[0] = 0 and offsets[B] = total_rows; each count must lie in
- * 1..255 (the per-question limit of "What is fused, precisely").
+/* Ragged batch: B questions with their own candidate counts, one launch
+ * (pull request "cuda: add a fused candidate-scoring kernel for CLM and
+ * Kev", "Verified on hardware", second group: batches of 1, 8, 4 and 3
+ * questions with K up to 255). Question b owns candidate rows
+ * offsets[b] .. offsets[b+1]-1 of candidates [total_rows][D] and the same
+ * slots of out [total_rows]; queries is [B][D]. offsets is a DEVICE array
+ * of B+1 int64 values with offsets[0] = 0 and offsets[B] = total_rows; each
+ * count must lie in 1..255 (the per-question limit of "What is fused,
+ * precisely").
  * The host checks pointers (offsets included), B, total_rows in
- * [B, 255*B] (else CS_ERR_K_RANGE), D, similarity, scale and temperature;
- * it cannot read device offsets without synchronizing, so each workgroup
- * checks its own question: a question whose offsets fall outside
- * [0, total_rows] or whose count is outside 1..255 is skipped, its output
- * slots are left untouched, and CS_ERR_K_RANGE is stored to *status (a
- * DEVICE int the caller sets to CS_OK beforehand; may be NULL). Each valid
- * question's result equals cs_score_candidates() on its own rows. One
- * workgroup per question; no workspace. */
+ * [B, 255*B] (else CS_ERR_K_RANGE), D, similarity, scale and temperature,
+ * then the workspace; it cannot read device offsets without synchronizing,
+ * so each workgroup checks its own question: a question whose offsets fall
+ * outside [0, total_rows] or whose count is outside 1..255 is skipped, its
+ * output slots are left untouched, and CS_ERR_K_RANGE is stored to *status
+ * (a DEVICE int the caller sets to CS_OK beforehand; may be NULL). Each
+ * valid question's result equals cs_score_candidates() on its own rows.
+ * Workspace: as for cs_score_candidates_batch(), optional, 8-byte aligned,
+ * zeroed once with cs_workspace_init() and left zeroed by every call, not
+ * shared by calls that may overlap. With one of cs_ragged_workspace_bytes()
+ * bytes, a small batch cuts every question into slices of the same number
+ * of rows (planned from the mean count total_rows / B), spread over the
+ * compute units and merged by the last slice of each question; without one,
+ * or when that size is 0, every question runs in one workgroup. */
 int cs_score_candidates_ragged(const float *queries, const float *candidates,
                                const int64_t *offsets, int B, int64_t total_rows, int D,
                                int similarity, float scale, float temperature, float *out,
-                               int *status, hipStream_t stream);
+                               int *status, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Workspace bytes a ragged call with these sizes uses: 0 when it runs one
+ * workgroup per question. Invalid sizes return 0. */
+size_t cs_ragged_workspace_bytes(int B, int64_t total_rows, int D, int similarity);
+
+/* The slicing cs_score_candidates_ragged() plans, with (has_workspace != 0)
+ * or without a workspace: rows per slice, and the most slices one question
+ * (255 rows) takes; a question of K_b rows takes ceil(K_b / rows_per_slice)
+ * slices. max_slices 1: one workgroup per question. Returns CS_OK or a
+ * size-validation status (as the call would). */
+int cs_plan_ragged(int B, int64_t total_rows, int D, int similarity, int has_workspace,
+                   int *rows_per_slice, int *max_slices);
 
 /* Projection + scoring: the caller-side heads fused with the scoring
  * (intro table of the page: CLM's state_head / action_head ahead of the

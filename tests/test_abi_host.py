@@ -230,7 +230,7 @@ def test_ragged_rejections_before_device_work(lib):
         a = dict(base, **kw)
         return lib.cs_score_candidates_ragged(a["q"], a["c"], a["o"], a["B"], a["T"], a["D"],
                                               a["sim"], a["scale"], a["temp"], a["out"], None,
-                                              None)
+                                              a.get("ws"), a.get("ws_bytes", 0), None)
 
     assert call(o=None) == cs.CS_ERR_NULL_POINTER
     assert call(q=None) == cs.CS_ERR_NULL_POINTER
@@ -242,6 +242,48 @@ def test_ragged_rejections_before_device_work(lib):
     assert call(scale=0.0) == cs.CS_ERR_SCALE
     assert call(temp=-1.0) == cs.CS_ERR_TEMPERATURE
     assert np.all(out == -7.0)
+    # a split plan needs a workspace of cs_ragged_workspace_bytes(), 8-byte aligned
+    qb, cb, ob = _host_buf(2560), _host_buf(255 * 2560), _host_buf(255)
+    one = np.array([0, 255], dtype=np.int64)
+    need = cs.cs_ragged_workspace_bytes(1, 255, 2560, "dot")
+    assert need > 0
+    ws = np.zeros(need + 64, dtype=np.uint8)
+    wsp = (ws.ctypes.data + 15) // 16 * 16
+    big = dict(q=qb.ctypes.data, c=cb.ctypes.data, o=one.ctypes.data, B=1, T=255, D=2560,
+               out=ob.ctypes.data)
+    assert call(**big, ws=wsp, ws_bytes=need - 1) == cs.CS_ERR_WORKSPACE
+    assert call(**big, ws=wsp + 4, ws_bytes=need) == cs.CS_ERR_WORKSPACE
+    assert call(**dict(big, D=0), ws=wsp, ws_bytes=need) == cs.CS_ERR_D_RANGE  # sizes first
+    assert np.all(ob == -7.0)
+
+
+def test_ragged_plan(lib):
+    """Ragged slicing is planned from the mean count, like a dense question
+    of that many rows, and never launches more slice workgroups than compute
+    units even when every question has 255 rows."""
+    # one question: the dense plan of the same question
+    st, rpg, slices = cs.cs_plan_ragged(1, 255, 2560, "dot", True)
+    G = cs.cs_plan_groups(1, 255, 2560, "dot", True)
+    assert st == 0 and slices == G and rpg == -(-255 // G)
+    # sixteen full questions: as the dense batch
+    st, rpg, slices = cs.cs_plan_ragged(16, 16 * 255, 2560, "dot", True)
+    G = cs.cs_plan_groups(16, 255, 2560, "dot", True)
+    assert st == 0 and slices == G
+    for B, rows, D in [(1, 40, 512), (3, 300, 2560), (8, 8 * 128, 2560), (16, 16 * 100, 1024),
+                       (100, 100 * 255, 2560), (2, 100, 40000)]:
+        st, rpg, slices = cs.cs_plan_ragged(B, rows, D, "cosine", True)
+        assert st == 0 and 1 <= slices <= 64 and rpg >= 1
+        assert slices == 1 or B * slices <= 256, (B, rows, D, rpg, slices)
+        if slices > 1:
+            assert slices == -(-255 // rpg)
+            assert cs.cs_ragged_workspace_bytes(B, rows, D, "cosine") == \
+                cs.cs_workspace_bytes_for_groups(B, slices)
+        else:
+            assert cs.cs_ragged_workspace_bytes(B, rows, D, "cosine") == 0
+    # a large batch, or no workspace: one workgroup per question
+    assert cs.cs_plan_ragged(1024, 1024 * 128, 2560, "dot", True)[2] == 1
+    assert cs.cs_plan_ragged(1, 255, 2560, "dot", False)[1:] == (255, 1)
+    assert cs.cs_plan_ragged(2, 1, 8, "dot", True)[0] == cs.CS_ERR_K_RANGE
 
 
 def test_projected_rejections_before_device_work(lib):

@@ -81,7 +81,7 @@ def _bits(b, dev):
     return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev)
 
 
-@pytest.mark.parametrize("kind", ["ragged", "projected_dot", "projected_cosine",
+@pytest.mark.parametrize("kind", ["ragged", "ragged_split", "projected_dot", "projected_cosine",
                                   "projected_dot_split", "projected_dot_split_tiles",
                                   "projected_cosine_slices"])
 def test_capture_multi_kernel_paths_replay_exact(cs, kind):
@@ -104,6 +104,24 @@ def test_capture_multi_kernel_paths_replay_exact(cs, kind):
             assert cs.cs_score_candidates_ragged(q, c, o, 300, rows, 520, "cosine",
                                                  float(workloads.SCALE_COSINE), 1.0, out,
                                                  status) == 0
+
+        shape = (rows,)
+    elif kind == "ragged_split":
+        # Eight questions of 1 to 255 rows, sliced over the chip and merged
+        # through the zeroed workspace, which every call leaves zero.
+        offsets = workloads.ragged_offsets(77, 8)
+        Q, C = workloads.ragged_inputs(78, offsets, 2560)
+        rows = int(offsets[-1])
+        q, c = torch.from_numpy(Q).to(dev), torch.from_numpy(C).to(dev)
+        o = torch.from_numpy(offsets).to(dev)
+        nbytes = cs.cs_ragged_workspace_bytes(8, rows, 2560, "dot")
+        assert nbytes > 0
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+        def run(out):
+            assert cs.cs_score_candidates_ragged(q, c, o, 8, rows, 2560, "dot",
+                                                 float(workloads.SCALE_DOT), 1.0, out, None, ws,
+                                                 nbytes) == 0
 
         shape = (rows,)
     else:

@@ -20,7 +20,9 @@ def note(msg):
     print(msg, flush=True)
 
 
-def run_ragged(cs, Q, C, offsets, sim, scale, status=None, out=None):
+def run_ragged(cs, Q, C, offsets, sim, scale, status=None, out=None, ws=None):
+    """One ragged call; ws: a zeroed uint8 device workspace (split plan) or
+    None (one workgroup per question)."""
     import torch
 
     dev = torch.device("cuda:0")
@@ -31,10 +33,19 @@ def run_ragged(cs, Q, C, offsets, sim, scale, status=None, out=None):
     if out is None:
         out = torch.full((total,), -5.0, device=dev)
     st = cs.cs_score_candidates_ragged(q, c, o, len(offsets) - 1, total, Q.shape[1], sim,
-                                       float(scale), 1.0, out, status)
+                                       float(scale), 1.0, out, status, ws,
+                                       0 if ws is None else ws.numel())
     assert st == 0, st
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def split_workspace(cs, B, total, D, sim):
+    import torch
+
+    n = cs.cs_ragged_workspace_bytes(B, total, D, sim)
+    assert n > 0, (B, total, D, sim)
+    return torch.zeros(n, dtype=torch.uint8, device=torch.device("cuda:0"))
 
 
 def check(p, want, offsets, label):
@@ -69,6 +80,95 @@ def test_ragged_edge_counts(cs, orc):
             check(p, want, offsets, f"counts={counts[:6]}")
             one = [b for b, k in enumerate(counts) if k == 1]
             assert all(p[offsets[b]] == 1.0 for b in one)
+
+
+# The page's batch-path cases: batches of 1, 8, 4 and 3 questions with K up
+# to 255 ("Verified on hardware", second group), here with counts that vary
+# per question, as a ragged batch spread over the chip.
+SPLIT_CASES = [
+    ([255], 2560, "dot"),
+    ([200, 3, 255, 17, 64, 128, 1, 90], 2560, "dot"),
+    ([255, 255, 254, 1], 512, "cosine"),
+    ([33, 255, 120], 1024, "cosine"),
+    ([255, 100, 7, 255, 60, 30, 2, 250], 1000, "cosine"),   # the general kernel
+    ([255, 9, 128], 4097, "dot"),                           # general kernel, q in two chunks
+    ([255] * 16, 2560, "dot"),
+]
+
+
+@pytest.mark.parametrize("counts,D,sim", SPLIT_CASES)
+def test_ragged_split_matches_oracle(cs, orc, counts, D, sim):
+    """Small ragged batches cut every question into slices of the planned
+    rows, over several workgroups merged by the question's last slice: the
+    oracle on every row, equal to the unsplit launch within fp32 rounding,
+    and the workspace zero again after each call."""
+    import torch
+
+    B = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    total = int(offsets[-1])
+    Q, C = workloads.ragged_inputs(211 + B + D, offsets, D)
+    scale = workloads.SCALE_COSINE if sim == "cosine" else workloads.SCALE_DOT
+    st, rpg, slices = cs.cs_plan_ragged(B, total, D, sim, True)
+    note(f"case ragged split counts={counts[:8]} D={D} {sim}: {rpg} rows per slice, "
+         f"up to {slices} slices")
+    assert st == 0 and slices > 1
+    want = orc.score_ragged(Q, C, offsets, sim, scale)
+    ws = split_workspace(cs, B, total, D, sim)
+    for rep in range(2):
+        p = run_ragged(cs, Q, C, offsets, sim, scale, ws=ws)
+        check(p, want, offsets, f"split rep={rep}")
+        assert np.all(p != -5.0)
+        assert int(torch.count_nonzero(ws)) == 0, "workspace left nonzero"
+    one = run_ragged(cs, Q, C, offsets, sim, scale)
+    assert float(np.max(np.abs(one.astype(np.float64) - p))) <= 2e-6
+    ones = [b for b, k in enumerate(counts) if k == 1]
+    assert all(p[offsets[b]] == 1.0 for b in ones)
+
+
+def test_ragged_split_bad_offsets(cs, orc):
+    """A question with invalid offsets is skipped by all of its slices (no
+    ticket drawn, nothing written) and flagged; the others merge normally
+    and the workspace returns to zero."""
+    import torch
+
+    D = 2560
+    # q0: 200 rows; q1: 0 rows (invalid); q2: 255 rows; q3: 300 rows (invalid)
+    offsets = np.array([0, 200, 200, 455, 755], dtype=np.int64)
+    total = 755
+    rng = np.random.default_rng(223)
+    Q = rng.standard_normal((4, D), dtype=np.float32)
+    C = rng.standard_normal((total, D), dtype=np.float32)
+    dev = torch.device("cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = split_workspace(cs, 4, total, D, "dot")
+    note("case ragged split bad offsets")
+    p = run_ragged(cs, Q, C, offsets, "dot", 0.0625, status=status, ws=ws)
+    assert int(status.item()) == cs.CS_ERR_K_RANGE
+    for b, (lo, hi) in {0: (0, 200), 2: (200, 455)}.items():
+        want = orc.score(Q[b], C[lo:hi], "dot", 0.0625)
+        assert np.max(np.abs(p[lo:hi].astype(np.float64) - want)) <= TOL
+    assert np.all(p[455:] == -5.0)
+    assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_ragged_split_equals_dense_split(cs, orc):
+    """Sixteen questions of 255 rows: the ragged plan cuts them as the dense
+    batch call does, and the results agree within fp32 rounding."""
+    import torch
+
+    B, K, D = 16, 255, 2560
+    Q, C = workloads.normal_inputs(227, B, K, D)
+    offsets = np.arange(B + 1, dtype=np.int64) * K
+    ws = split_workspace(cs, B, B * K, D, "dot")
+    p = run_ragged(cs, Q, C.reshape(B * K, D), offsets, "dot", 0.0625, ws=ws)
+    dev = torch.device("cuda:0")
+    dense = cs.score(torch.from_numpy(Q).to(dev), torch.from_numpy(C).to(dev), "dot", 0.0625)
+    torch.cuda.synchronize()
+    d = dense.cpu().numpy().reshape(-1)
+    assert float(np.max(np.abs(p.astype(np.float64) - d))) <= 2e-6
+    check(p, orc.score_ragged(Q, C.reshape(B * K, D), offsets, "dot", 0.0625), offsets,
+          "16 x 255 ragged split")
 
 
 def test_ragged_equal_counts_equals_dense(cs):
