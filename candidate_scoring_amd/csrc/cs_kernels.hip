@@ -124,6 +124,15 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
         for (int r = 0; r < R; ++r)
           c[r][j] = (FULL || idx < D4) ? load4<NT>(rows[r] + idx) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      // Every load of the row group is issued before the first product.
+      // Left alone, the scheduler interleaves loads and products to save
+      // registers (103 instead of 161 VGPRs for the Kev shape, about 3
+      // loads in flight instead of 20). The large batch then hides that
+      // with more resident waves, but a split question's slice has only one
+      // 4-wave workgroup per compute unit: 16 questions of 255 x 2560 took
+      // 20.0 us instead of 14.2 us, with no change for the 1024-question
+      // batch (384.5 / 385.1 us).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
 #pragma unroll
