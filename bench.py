@@ -684,7 +684,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "occupancy_percent": committed_occupancy(),
-                     "kernel": "fused_regq<dot, nv=10, rows=2, full, nontemporal>",
+                     "kernel": devc.cs.cs_plan_kernel(w.B, w.K, w.D, w.similarity, True)[1],
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
     }
     if not args.no_latency:

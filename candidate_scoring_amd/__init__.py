@@ -71,6 +71,7 @@ def load(path: Path | str = LIBRARY):
         "cs_plan_groups": (i32, [i32, i32, i32, i32, i32]),
         "cs_plan_launch": (i32, [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_uint),
                                  ctypes.POINTER(ctypes.c_uint), ctypes.POINTER(ctypes.c_int)]),
+        "cs_plan_kernel": (i32, [i32, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]),
         "cs_score_candidates": (i32, [vp, vp, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
         "cs_score_candidates_batch": (i32, [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
         "cs_score_candidates_batch_groups": (
@@ -202,6 +203,15 @@ def cs_plan_launch(B: int, K: int, D: int, similarity, has_workspace: bool,
                                int(bool(aligned16)), ctypes.byref(grid), ctypes.byref(block),
                                ctypes.byref(groups))
     return st, grid.value, block.value, groups.value
+
+
+def cs_plan_kernel(B: int, K: int, D: int, similarity, has_workspace: bool,
+                   aligned16: bool = True):
+    """(status, name) of the kernel instantiation the batch call would launch."""
+    buf = ctypes.create_string_buffer(256)
+    st = load().cs_plan_kernel(B, K, D, _sim(similarity), int(bool(has_workspace)),
+                               int(bool(aligned16)), buf, len(buf))
+    return st, buf.value.decode()
 
 
 def cs_score_candidates(query, candidates, K: int, D: int, similarity, scale: float,

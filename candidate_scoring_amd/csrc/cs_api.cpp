@@ -14,6 +14,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <algorithm>
@@ -220,9 +221,11 @@ cs::LaunchShape make_shape(int B, int K, int D, int G, int rpg, const void* Q, c
   return ls;
 }
 
+// ws_in_library: the workspace is the library's own static array (the entry
+// point that allocates nothing), which the debug pointer check skips.
 int score(const float* Q, const float* C, int B, int K, int D, int sim, float scale,
           float temperature, float* out, void* ws, size_t ws_bytes, int groups,
-          hipStream_t stream) {
+          hipStream_t stream, bool ws_in_library = false) {
   int st = validate(Q, C, out, B, K, D, sim, scale, temperature);
   if (st != CS_OK) return st;
   if (groups < 1 || groups > K) return CS_ERR_WORKSPACE;
@@ -236,7 +239,7 @@ int score(const float* Q, const float* C, int B, int K, int D, int sim, float sc
   }
   if (debug_pointers()) {
     if (!is_device_pointer(Q) || !is_device_pointer(C) || !is_device_pointer(out) ||
-        (G > 1 && !is_device_pointer(ws)))
+        (G > 1 && !ws_in_library && !is_device_pointer(ws)))
       return CS_ERR_HOST_POINTER;
   }
 
@@ -501,8 +504,9 @@ int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace) {
 
 int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
                    unsigned* grid, unsigned* block, int* groups) {
+  const int st = validate(&B, &B, &B, B, K, D, similarity, 1.0f, 1.0f);
+  if (st != CS_OK) return st;
   const int G = cs_plan_groups(B, K, D, similarity, has_workspace);
-  if (G < 1) return CS_ERR_K_RANGE;
   const int rpg = (K + G - 1) / G;
   // 16-byte aligned or deliberately misaligned dummy addresses
   const void* p = reinterpret_cast<const void*>(uintptr_t(aligned16 ? 256 : 260));
@@ -511,6 +515,29 @@ int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int a
   if (block) *block = ls.block;
   if (groups) *groups = G;
   return CS_OK;
+}
+
+int cs_plan_kernel(int B, int K, int D, int similarity, int has_workspace, int aligned16,
+                   char* name, size_t name_bytes) {
+  const int st = validate(&B, &B, &B, B, K, D, similarity, 1.0f, 1.0f);
+  if (st != CS_OK) return st;
+  const int G = cs_plan_groups(B, K, D, similarity, has_workspace);
+  if (name == nullptr || name_bytes == 0) return CS_ERR_NULL_POINTER;
+  const int rpg = (K + G - 1) / G;
+  const void* p = reinterpret_cast<const void*>(uintptr_t(aligned16 ? 256 : 260));
+  const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, p, p);
+  const char* sim = similarity == CS_SIM_COSINE ? "cosine" : "dot";
+  const char* nt = ls.nt ? "non-temporal" : "cached";
+  const char* mode = G > 1 ? "split" : "one workgroup per question";
+  int n;
+  if (ls.nv > 0)
+    n = snprintf(name, name_bytes, "fused_regq<%s, %d pieces/lane, %d rows/wave, %s, %s, %s>",
+                 sim, ls.nv, cs::regq_rows_per_wave(ls.nv),
+                 D / 4 == ls.nv * 64 ? "full" : "partial", nt, mode);
+  else
+    n = snprintf(name, name_bytes, "fused_general<%s, %s, %s, %s>", sim,
+                 ls.vec == 4 ? "16-byte pieces" : "scalar", nt, mode);
+  return n >= 0 && (size_t)n < name_bytes ? CS_OK : CS_ERR_WORKSPACE;
 }
 
 size_t cs_workspace_bytes_for_groups(int B, int groups) {
@@ -570,7 +597,7 @@ int cs_score_candidates_batch_noalloc(const float* queries, const float* candida
     return CS_ERR_LAUNCH;
   }
   return score(queries, candidates, B, K, D, similarity, scale, temperature, out, ws, need, G,
-               stream);
+               stream, /*ws_in_library=*/true);
 }
 
 int cs_score_candidates_unfused(const float* queries, const float* candidates, int B, int K,

@@ -82,49 +82,80 @@ extern "C" {
 #define CS_ERR_HOST_POINTER (-10) /* only with CS_DEBUG_POINTERS=1: a pointer is not device memory */
 #define CS_ERR_UNSUPPORTED (-11) /* valid sizes this entry point does not implement (see its comment) */
 
-/* Returns CS_ABI_VERSION. */
+/* Returns CS_ABI_VERSION: 1, the abi_version the page's manifest records
+ * ("The manifest, and CI"). */
 int cs_abi_version(void);
 
-/* Static, human-readable text for a status code (never NULL). */
+/* Static, human-readable text for a status code (never NULL). The codes are
+ * the rejections of "Verified on hardware", third group, and this library's
+ * readings listed above. */
 const char *cs_status_string(int status);
 
-/* The hipError_t of this thread's last CS_ERR_LAUNCH (0 if none). */
+/* The hipError_t of this thread's last CS_ERR_LAUNCH (0 if none). The
+ * library's own addition: the page names no launch-failure code. */
 int cs_last_hip_error(void);
 
 /* Workspace bytes the planned launch needs for B questions of K candidates
  * of length D with the given similarity; 0 when that plan runs one
- * workgroup per question and needs none. Invalid sizes return 0. */
+ * workgroup per question and needs none. Invalid sizes return 0. The
+ * workspace serves the whole-chip split of small batches: the page's own
+ * finding ("What it is worth") is that one block per question leaves a
+ * single question on one compute unit. The similarity is an argument so
+ * that every size function validates the same argument set as the call. */
 size_t cs_workspace_bytes(int B, int K, int D, int similarity);
 
-/* Workspace bytes for an explicit number of workgroups per question. */
+/* Workspace bytes for an explicit number of workgroups per question (for
+ * cs_score_candidates_batch_groups()). */
 size_t cs_workspace_bytes_for_groups(int B, int groups);
 
 /* Zero `bytes` bytes of `workspace` with a kernel on `stream` (no memset
- * node, no synchronization). Returns CS_OK, CS_ERR_NULL_POINTER or
- * CS_ERR_LAUNCH. */
+ * node, no synchronization, so it may also be captured: "Verified on
+ * hardware", fourth group, asks that calls capture cleanly). Returns CS_OK,
+ * CS_ERR_NULL_POINTER or CS_ERR_LAUNCH. */
 int cs_workspace_init(void *workspace, size_t bytes, hipStream_t stream);
 
 /* Workgroups per question that cs_score_candidates_batch() would launch for
  * these sizes, with (has_workspace != 0) or without a workspace. Both entry
  * points use this same pure function, so a single-question call and a
- * batch of one pick the same kernel and give bitwise the same result. */
+ * batch of one pick the same kernel and give bitwise the same result (the
+ * agreement "Verified on hardware", second group, asks for). The planned
+ * count depends on the current device's compute-unit count. */
 int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace);
 
 /* The launch cs_score_candidates_batch() would make for these sizes: grid
  * (workgroups), block (threads) and workgroups per question, for pointers
  * that are (aligned16 != 0) or are not 16-byte aligned. Returns CS_OK or a
- * size-validation status. For benches that time a matching empty kernel. */
+ * size-validation status. For benches that time a matching empty kernel:
+ * the launch-bound floor of "What it is worth", graph paragraph. */
 int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
                    unsigned *grid, unsigned *block, int *groups);
 
+/* Writes to name (name_bytes long, NUL-terminated) a description of the
+ * kernel instantiation cs_score_candidates_batch() launches for these sizes:
+ * kernel, similarity, pieces per lane and rows per wave, cached or
+ * non-temporal loads, split or not. For reports that label measurements
+ * by the code that ran. Returns CS_OK, a size-validation status,
+ * CS_ERR_NULL_POINTER, or CS_ERR_WORKSPACE if name_bytes is too short. */
+int cs_plan_kernel(int B, int K, int D, int similarity, int has_workspace, int aligned16,
+                   char *name, size_t name_bytes);
+
 /* One question: query [D], candidates [K][D], out [K] (device, fp32).
- * Equivalent to cs_score_candidates_batch() with B = 1. */
+ * Equivalent to cs_score_candidates_batch() with B = 1, bitwise.
+ * Source: pull request "cuda: add a fused candidate-scoring kernel for CLM and Kev", "Verified on hardware", second group (the single-question
+ * entry point, which must agree with the batch path) and fourth group (a
+ * call queues on the caller's stream, never synchronizes, and captures as
+ * one graph node that replays to the same result); "What is fused,
+ * precisely" for what is computed. */
 int cs_score_candidates(const float *query, const float *candidates, int K, int D,
                         int similarity, float scale, float temperature, float *out,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* B independent questions in one launch: queries [B][D], candidates
- * [B][K][D], out [B][K] (device, fp32). */
+ * [B][K][D], out [B][K] (device, fp32). Source: pull request "cuda: add a fused candidate-scoring kernel for CLM and Kev", "Verified on
+ * hardware", second group (the batch entry point: batches of 1, 8, 4 and 3
+ * questions agree with single calls) and fourth group (one graph node,
+ * replayed exactly); "What is fused, precisely" (a batch is a grid over
+ * questions). */
 int cs_score_candidates_batch(const float *queries, const float *candidates, int B, int K,
                               int D, int similarity, float scale, float temperature,
                               float *out, void *workspace, size_t workspace_bytes,
@@ -132,8 +163,9 @@ int cs_score_candidates_batch(const float *queries, const float *candidates, int
 
 /* As cs_score_candidates_batch(), with the number of workgroups per
  * question given explicitly (1 <= groups <= K; groups > 1 needs a workspace
- * of cs_workspace_bytes_for_groups(B, groups) bytes). For tuning and tests;
- * the distribution does not depend on groups beyond fp32 rounding. */
+ * of cs_workspace_bytes_for_groups(B, groups) bytes; a count that would
+ * leave a slice empty is CS_ERR_WORKSPACE). For tuning and tests; the
+ * distribution does not depend on groups beyond fp32 rounding. */
 int cs_score_candidates_batch_groups(const float *queries, const float *candidates, int B,
                                      int K, int D, int similarity, float scale,
                                      float temperature, float *out, void *workspace,

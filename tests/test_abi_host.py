@@ -257,6 +257,23 @@ def test_ragged_rejections_before_device_work(lib):
     assert np.all(ob == -7.0)
 
 
+def test_plan_queries_name_the_launch(lib):
+    """cs_plan_kernel names the instantiation the batch call launches (the
+    bench labels its roofline with it); both plan queries return the
+    argument checks' status for invalid sizes."""
+    st, name = cs.cs_plan_kernel(1024, 255, 2560, "dot", True)
+    assert st == 0 and name.startswith("fused_regq<dot, 10 pieces/lane, 2 rows/wave, full")
+    assert "non-temporal" in name and "one workgroup per question" in name
+    st, name = cs.cs_plan_kernel(1, 255, 512, "cosine", True)
+    assert st == 0 and name.startswith("fused_regq<cosine") and name.endswith("split>")
+    st, name = cs.cs_plan_kernel(3, 255, 1000, "cosine", True, aligned16=False)
+    assert st == 0 and name.startswith("fused_general<cosine, scalar")
+    assert cs.cs_plan_kernel(0, 255, 512, "dot", True)[0] == cs.CS_ERR_BATCH
+    assert cs.cs_plan_kernel(1, 256, 512, "dot", True)[0] == cs.CS_ERR_K_RANGE
+    assert cs.cs_plan_launch(1, 255, 0, "dot", True)[0] == cs.CS_ERR_D_RANGE
+    assert cs.cs_plan_launch(1, 255, 8, 7, True)[0] == cs.CS_ERR_SIMILARITY
+
+
 def test_ragged_plan(lib):
     """Ragged slicing is planned from the mean count, like a dense question
     of that many rows, and never launches more slice workgroups than compute
