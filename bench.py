@@ -264,6 +264,103 @@ def phase_clock_section(devc, calls=200, reps=40):
     return res
 
 
+def projected_phase_section(devc, calls=6, reps=12):
+    """Where the Kev projection call's time goes: the measurement build's
+    clocks in its three launches (query projection, fold, bf16 candidate
+    pass) for the last of `calls` back-to-back calls, `reps` times; medians
+    over repetitions of each phase (per-workgroup phases as the median over
+    workgroups), of the gaps between launches and of when the candidate
+    pass's workgroups end, by dispatch order (blockIdx // 256) and by
+    blockIdx mod 8 (the XCD under round-robin dispatch)."""
+    torch, cs = devc.torch, devc.cs
+    lib = cs.load()
+    name = "kev_proj_dot_batch1024_255x2560_p256"
+    w = workloads.make_projected(name)
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(devc.dev)
+
+    xq, xc, wq, wc = dev16(w.xq_bits), dev16(w.xc_bits), dev16(w.wq_bits), dev16(w.wc_bits)
+    out = torch.empty(w.B, w.K, dtype=torch.float32, device=devc.dev)
+    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, w.similarity)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=devc.dev)
+
+    def once():
+        st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, w.similarity,
+                                   float(w.scale), 1.0, out, ws, nbytes, devc.stream)
+        assert st == 0, st
+
+    regions, wgs, slots = 4, 1024, 16
+    buf = np.zeros(regions * wgs * slots, dtype=np.uint64)
+    fields = {}
+    nfold = None
+    for _ in range(reps):
+        for _ in range(calls):
+            once()
+        torch.cuda.synchronize()
+        if lib.cs_projected_phase_clocks_read(ctypes.c_void_p(buf.ctypes.data), buf.nbytes) != 0:
+            raise RuntimeError("cs_projected_phase_clocks_read failed")
+        T = buf.reshape(regions, wgs, slots).astype(np.int64)
+        proj, fold, cand = T[1, :256], T[2], T[3]
+        if nfold is None:
+            # workgroups of each launch: the ones stamped by this call
+            nfold = int(np.count_nonzero(fold[:, 2] >= proj[:, 0].min()))
+            ncand = int(np.count_nonzero(cand[:, 5] >= proj[:, 0].min()))
+        fold, cand = fold[:nfold], cand[:ncand]
+        if not (proj[:, 0].min() > 0 and nfold > 0 and cand[:, 5].min() > 0):
+            raise RuntimeError("no phase clocks recorded: the calls did not reach libcs_phase.so")
+        t0 = proj[:, 0].min()
+        us = lambda v: float(v) * PHASE_TICK_US
+        med = lambda a, b, x: us(np.median(x[:, b] - x[:, a]))
+        cend = cand[:, 5] - cand[:, 0].min()
+        # Bytes streamed while every workgroup of the pass is running: each
+        # workgroup's progress interpolated between its stamps (u staged,
+        # a quarter, half, three quarters of its rows, exit).
+        marks = np.stack([cand[:, 1], cand[:, 2], cand[:, 3], cand[:, 4], cand[:, 5]], axis=1)
+        ta, tb = np.median(cand[:, 1]), cand[:, 5].min()
+        frac = np.array([0.0, 0.25, 0.5, 0.75, 1.0])
+        done = sum(np.interp(tb, m, frac) - np.interp(ta, m, frac) for m in marks.astype(np.float64))
+        qbytes = 2.0 * w.K * w.Hc * w.B / ncand  # bytes per workgroup
+        row = {
+            "query projection: contraction, wave 0": med(0, 1, proj),
+            "query projection: wait for the other waves": med(1, 2, proj),
+            "query projection: q' and parts stored": med(2, 3, proj),
+            "query projection: W^T share packed": med(3, 4, proj),
+            "query projection: span": us(proj[:, 4].max() - t0),
+            "gap, projection to fold": us(fold[:, 0].min() - proj[:, 4].max()),
+            "fold: contraction, wave 0": med(0, 1, fold),
+            "fold: u stored": med(1, 2, fold),
+            "fold: span": us(fold[:, 2].max() - fold[:, 0].min()),
+            "gap, fold to candidate pass": us(cand[:, 0].min() - fold[:, 2].max()),
+            "candidate pass: u staged": med(0, 1, cand),
+            "candidate pass: first workgroup done": us(cend.min()),
+            "candidate pass: TB/s while every workgroup runs":
+                done * qbytes / (us(tb - ta) * 1e-6) / 1e12,
+            "candidate pass: median workgroup done": us(np.median(cend)),
+            "candidate pass: span": us(cend.max()),
+            "call span": us(cand[:, 5].max() - t0),
+        }
+        for r in range(ncand // 256):
+            sel = slice(256 * r, 256 * (r + 1))
+            row[f"candidate pass: workgroups {256 * r}-{256 * r + 255} done, median"] = \
+                us(np.median(cend[sel]))
+        for x in range(8):
+            row[f"candidate pass: blockIdx mod 8 = {x} done, median"] = \
+                us(np.median(cend[np.arange(ncand) % 8 == x]))
+        row["candidate pass: workgroups done, 10th percentile"] = us(np.percentile(cend, 10))
+        row["candidate pass: workgroups done, 90th percentile"] = us(np.percentile(cend, 90))
+        for k, v in row.items():
+            fields.setdefault(k, []).append(v)
+    res = {"workload": name, "B": w.B, "K": w.K, "Hq": w.Hq, "Hc": w.Hc, "P": w.P,
+           "fold_workgroups": nfold, "candidate_pass_workgroups": ncand, "calls": calls,
+           "reps": reps}
+    res.update({k + ("" if "TB/s" in k else " us"): round(float(np.median(v)), 3)
+                for k, v in fields.items()})
+    log(f"projected phase clocks: {res}")
+    del xq, xc, wq, wc, out, ws
+    return res
+
+
 def ab_section(devc, iters, headline=None):
     """Fused vs the unfused baseline (separate norm pass + scoring that loads
     the staged norms) on the page's results-table shapes and the Kev batch.
@@ -593,7 +690,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--phase-clocks", action="store_true",
-                    help="only the per-phase clocks of the split calls, from the measurement "
+                    help="only the per-phase clocks of the split calls and of the Kev "
+                         "projection call, from the measurement "
                          "build candidate_scoring_amd/libcs_phase.so (python -m "
                          "candidate_scoring_amd.build --phase-clocks)")
     args = ap.parse_args()
@@ -611,10 +709,12 @@ def main():
         # rather than to libcs.so, which it names as a dependency.
         ctypes.CDLL(str(cs_pkg.PKG / "libcs_phase.so"), mode=ctypes.RTLD_GLOBAL)
         lib = cs_pkg.load(cs_pkg.PKG / "libcs_phase.so")
-        lib.cs_phase_clocks_read.restype = ctypes.c_int
-        lib.cs_phase_clocks_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        for fn in (lib.cs_phase_clocks_read, lib.cs_projected_phase_clocks_read):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
         devc = Device()
         print(json.dumps({"phase_clocks": phase_clock_section(devc),
+                          "projected_phase_clocks": projected_phase_section(devc),
                           "library": "libcs_phase.so (measurement build)"}), flush=True)
         return
 

@@ -23,27 +23,32 @@ namespace {
 
 // Phase clocks: a build with CS_PHASE_CLOCKS defined (libcs_phase.so, a
 // measurement build, never the product library) makes thread 0 of each
-// workgroup store the 100 MHz device clock at fixed points of the scoring
-// kernels and the split merge; in every other build CS_PHASE expands to
-// nothing. Slots: 0 start, 1 rows reduced (wave 0), 2 after the barrier,
-// 3 softmax stored, 4 release fence done, 5 ticket drawn, 6 after the
-// ticket barrier, 7 acquire done (last slice), 8 merge factors ready,
-// 9 rescaled and reset, 10 workgroup exit.
+// workgroup store the 100 MHz device clock at fixed points of a kernel; in
+// every other build CS_PHASE and CS_PHASE_IN expand to nothing. Each source
+// file keeps its own clock array (region-major, then workgroup, 16 slots).
+// Region 0, the scoring kernels and the split merge: 0 start, 1 rows
+// reduced (wave 0), 2 after the barrier, 3 softmax stored, 4 release fence
+// done, 5 ticket drawn, 6 after the ticket barrier, 7 acquire done (last
+// slice), 8 merge factors ready, 9 rescaled and reset, 10 workgroup exit.
+// Regions 1-3 belong to the dot projection's three launches and list their
+// slots where they are stamped.
 #ifdef CS_PHASE_CLOCKS
 constexpr int kPhaseWorkgroups = 1024;
 constexpr int kPhaseSlots = 16;
-__device__ unsigned long long g_phase_clk[kPhaseWorkgroups * kPhaseSlots];
-#define CS_PHASE(slot)                                                                    \
+constexpr int kPhaseRegions = 4;
+__device__ unsigned long long g_phase_clk[kPhaseRegions * kPhaseWorkgroups * kPhaseSlots];
+#define CS_PHASE_IN(region, slot)                                                         \
   do {                                                                                    \
     if (threadIdx.x == 0 && blockIdx.x < (unsigned)::cs::kPhaseWorkgroups)                \
-      ::cs::g_phase_clk[blockIdx.x * ::cs::kPhaseSlots + (slot)] =                          \
-          __builtin_amdgcn_s_memrealtime();                                               \
+      ::cs::g_phase_clk[((region) * ::cs::kPhaseWorkgroups + blockIdx.x) *                \
+                            ::cs::kPhaseSlots + (slot)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #else
-#define CS_PHASE(slot) \
-  do {                 \
+#define CS_PHASE_IN(region, slot) \
+  do {                            \
   } while (0)
 #endif
+#define CS_PHASE(slot) CS_PHASE_IN(0, slot)
 
 
 constexpr int kWave = 64;

@@ -478,7 +478,7 @@ extern "C" int cs_phase_clocks_read(void* dst, size_t bytes) {
                                   hipMemcpyDeviceToHost);
 }
 extern "C" int cs_phase_clocks_clear(void) {
-  static unsigned long long zeros[cs::kPhaseWorkgroups * cs::kPhaseSlots];
+  static unsigned long long zeros[cs::kPhaseRegions * cs::kPhaseWorkgroups * cs::kPhaseSlots];
   return (int)hipMemcpyToSymbol(HIP_SYMBOL(cs::g_phase_clk), zeros, sizeof(zeros), 0,
                                 hipMemcpyHostToDevice);
 }

@@ -204,6 +204,9 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     uint16_t* __restrict__ wpack, int Hc, unsigned* __restrict__ tickets, long long ntiles) {
   __shared__ float part[kPqWaves][16][kWave];
   __shared__ uint4 stage[kPqWaves][2][4][kWave];  // [wave][slot][x0, x1, w0, w1][lane]
+  // Phase clocks (region 1): 0 start, 1 wave 0's partial tile in LDS, 2 after
+  // the barrier, 3 q' and its parts stored, 4 exit (W^T share packed).
+  CS_PHASE_IN(1, 0);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int ptiles = (P + 31) / 32;
   // Consecutive workgroups go to different XCDs (each with its own L2), so
@@ -298,7 +301,9 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) part[wave][4 * (2 * rb + cb) + i][lane] = acc4[rb][cb][i];
+    CS_PHASE_IN(1, 1);
     __syncthreads();
+    CS_PHASE_IN(1, 2);
     // Element i of tile (rb, cb) in lane l is q'[b0 + 16*rb + 4*(l/16) + i][p0 + 16*cb + l%16].
     for (int e = wave; e < 16; e += kPqWaves) {
       float v = 0.0f;
@@ -322,6 +327,7 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
     // of each 32-question block clears its questions' tickets (the candidate
     // pass runs two launches later on the same stream).
     if (tickets != nullptr && p0 == 0 && tid < 32 && b0 + tid < B) tickets[b0 + tid] = 0u;
+    CS_PHASE_IN(1, 3);
   }
   if (wpack != nullptr) {
     // This workgroup's share of the fold's W^T packing (independent of q'),
@@ -333,6 +339,7 @@ __global__ __launch_bounds__(kPqWaves * kWave) void proj_query_mfma(
          t += blockDim.x)
       pack_wt_block(wc, wpack, Hc, P, t);
   }
+  CS_PHASE_IN(1, 4);
 }
 
 // u[b][h] = sum_p q'[b][p] * w[p][h]  (q' [B][P] fp32, w [P][H] bf16,
@@ -351,6 +358,9 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
                                                        const uint16_t* __restrict__ wp,
                                                        float* __restrict__ u, int B, int H,
                                                        int P) {
+  // Phase clocks (region 2, both folds): 0 start, 1 wave 0's contraction
+  // done, 2 exit.
+  CS_PHASE_IN(2, 0);
   const int lane = threadIdx.x & (kWave - 1);
   // Workgroups numbered per XCD, as in proj_query_mfma: XCD j takes a run of
   // question blocks and reads only their parts from its own L2.
@@ -396,6 +406,7 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
       }
     }
   }
+  CS_PHASE_IN(2, 1);
   // Accumulator e of lane l: question 32*qb + 8*(e/4) + 4*(l/32) + e%4,
   // column 32*(hg*4 + nb) + l%32.
 #pragma unroll
@@ -408,6 +419,7 @@ __global__ __launch_bounds__(256) void fold_query_mfma(const uint16_t* __restric
       if (b < B) u[(size_t)b * (size_t)H + hcol] = acc[nb][e];
     }
   }
+  CS_PHASE_IN(2, 2);
 }
 
 // The same fold for batches too small to fill the chip: with few question
@@ -425,6 +437,7 @@ __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split
   // Partial tiles as four float4 rows per block, lane-contiguous, so each
   // 16-byte LDS access of a wave covers consecutive banks.
   __shared__ float4 red[kFoldSplitWaves][kFoldNb][4][kWave];
+  CS_PHASE_IN(2, 0);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int hgroups = (H + 32 * kFoldNb - 1) / (32 * kFoldNb);
   const long long qb = blockIdx.x / hgroups;
@@ -467,6 +480,7 @@ __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split
     for (int j = 0; j < 4; ++j)
       red[wave][nb][j][lane] =
           make_float4(acc[nb][4 * j], acc[nb][4 * j + 1], acc[nb][4 * j + 2], acc[nb][4 * j + 3]);
+  CS_PHASE_IN(2, 1);
   __syncthreads();
   // Wave w sums and stores column block w (kFoldNb == kFoldSplitWaves).
   const int nb = wave;
@@ -495,6 +509,7 @@ __global__ __launch_bounds__(kFoldSplitWaves * kWave) void fold_query_mfma_split
       if (b < B) u[(size_t)b * (size_t)H + hcol] = sum[e];
     }
   }
+  CS_PHASE_IN(2, 2);
 }
 static_assert(kFoldNb == kFoldSplitWaves, "one column block per wave in the split fold's sum");
 
@@ -657,6 +672,9 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
                                                          const float* __restrict__ u) {
   __shared__ Lds s;
   __shared__ float4 us_lo[8 * kWave], us_hi[8 * kWave];
+  // Phase clocks (region 3): 0 start, 1 u staged in LDS, 2-4 wave 0 past a
+  // quarter, half and three quarters of the slice's rows, 5 exit.
+  CS_PHASE_IN(3, 0);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int pieces = a.D >> 3;
@@ -680,8 +698,18 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
       us_hi[idx] = u1;
     }
     __syncthreads();
+    CS_PHASE_IN(3, 1);
     const uint16_t* Xb = xc + qn.row * (size_t)a.D;
+#ifdef CS_PHASE_CLOCKS
+    int quarter = 1;
+#endif
     for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
+#ifdef CS_PHASE_CLOCKS
+      if (quarter <= 3 && 4 * (k0 - r0) >= quarter * (r1 - r0)) {
+        CS_PHASE_IN(3, 1 + quarter);
+        ++quarter;
+      }
+#endif
       float acc[R];
       const uint16_t* rows[R];
 #pragma unroll
@@ -713,6 +741,7 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
     if (G > 1) split_merge(s, a, qn, b, tid, lane, wave, G);
     __syncthreads();
   }
+  CS_PHASE_IN(3, 5);
 }
 
 // Epilogue of the cosine tile: each row of C' reduced to c'.q' and |c'|^2,
@@ -1499,3 +1528,12 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
 }
 
 }  // namespace cs
+
+#ifdef CS_PHASE_CLOCKS
+// Measurement build only: the phase clocks of this file's kernels (regions
+// 1-3, same layout as cs_phase_clocks_read), copied to host memory.
+extern "C" int cs_projected_phase_clocks_read(void* dst, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(cs::g_phase_clk), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif

@@ -98,6 +98,10 @@ def dev(cs):
     (9, 250, 64, 128, 64, "cosine"),       # one question more: the tile kernel
     (256, 32, 64, 136, 64, "cosine"),      # unsplit questions: one workgroup per compute unit
     (257, 32, 64, 136, 64, "cosine"),      # one question more: the tile kernel
+    (1027, 37, 64, 1000, 96, "dot"),       # more candidate-pass workgroups than stay
+                                           # resident; partial pieces per lane
+    (1025, 255, 64, 512, 64, "dot"),       # 32 question blocks and one more
+    (1024, 1, 8, 8, 8, "dot"),             # one row per question: most waves get none
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
