@@ -29,7 +29,8 @@ namespace {
 // Region 0, the scoring kernels and the split merge: 0 start, 1 rows
 // reduced (wave 0), 2 after the barrier, 3 softmax stored, 4 release fence
 // done, 5 ticket drawn, 6 after the ticket barrier, 7 acquire done (last
-// slice), 8 merge factors ready, 9 rescaled and reset, 10 workgroup exit.
+// slice), 8 merge factors ready, 9 rescaled and reset, 10 workgroup exit,
+// 11-13 wave 0 past a quarter, half and three quarters of the slice's rows.
 // Regions 1-3 belong to the dot projection's three launches and list their
 // slots where they are stamped.
 #ifdef CS_PHASE_CLOCKS
@@ -234,6 +235,7 @@ struct Lds {
   int hist[kMaxSlots];        // ragged longest-first order: questions per count
   int wave_sum[kBlock / kWave];
   int pick[2];
+  int next_group;             // the next row group of the slice not yet handed out
 };
 
 // Where one question's candidates and outputs live: rows row .. row+K-1 of
@@ -242,6 +244,21 @@ struct Question {
   size_t row;
   int K;
 };
+
+// Row groups of a slice are handed to the waves of a workgroup as they go:
+// wave w starts with group w, and each wave draws its next group from an LDS
+// counter (set to the wave count before the slice) while its current loads
+// are in flight. With a fixed share per wave the memory pipeline, which
+// serves older waves first, left wave 0 of the fp32 Kev batch done 21 us
+// before the last wave of its workgroup, out of a 91 us workgroup; the
+// compute unit then streamed with ever fewer waves. Which wave takes a row
+// does not change how the row is reduced, so the results do not depend on
+// the order.
+__device__ __forceinline__ int draw_group(Lds& s, int lane) {
+  int g = 0;
+  if (lane == 0) g = atomicAdd(&s.next_group, 1);
+  return __builtin_amdgcn_readfirstlane(g);
+}
 
 // Resolves question b. For a ragged batch the workgroup checks the offsets
 // it was given (0 <= lo, hi <= total rows, 1 <= hi - lo <= 255); a bad

@@ -74,7 +74,7 @@ namespace {
 // hot loop; the query's squared norm is reduced once per workgroup (by wave
 // 0, which holds all of q) right before the softmax.
 
-template <bool COS, int NV, int R, bool FULL, bool NT, int MODE>
+template <bool COS, int NV, int R, bool FULL, bool NT, int MODE, bool DRAWN>
 __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -84,6 +84,16 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
   const int G = MODE == kRagged ? 1 : a.G;
   const long long items = (long long)a.B * G;
   CS_PHASE(0);
+  // DRAWN (unsplit questions): row groups come from the LDS counter. The
+  // slices of a split question hold one or two groups per wave and keep a
+  // fixed share; compiled apart, so their code is unchanged (with the
+  // counter's barrier and draws a 16-question split call measured 3-5 %
+  // slower).
+  constexpr bool drawn = DRAWN;
+  if constexpr (drawn) {
+    if (tid == 0) s.next_group = nwaves;
+    __syncthreads();
+  }
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     int b = (int)(item / G);
     if constexpr (MODE == kRagged) {
@@ -107,7 +117,16 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
     }
 
     const float* Cb = a.C + qn.row * (size_t)a.D;
-    for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
+#ifdef CS_PHASE_CLOCKS
+    int quarter = 1;
+#endif
+    for (int k0 = r0 + wave * R; k0 < r1;) {
+#ifdef CS_PHASE_CLOCKS
+      if (quarter <= 3 && 4 * (k0 - r0) >= quarter * (r1 - r0)) {
+        CS_PHASE(10 + quarter);
+        ++quarter;
+      }
+#endif
       constexpr int V = COS ? 2 * R : R;
       float acc[V];
 #pragma unroll
@@ -133,6 +152,7 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
       // 20.0 us instead of 14.2 us, with no change for the 1024-question
       // batch (384.5 / 385.1 us).
       __builtin_amdgcn_sched_barrier(0);
+      const int next = drawn ? draw_group(s, lane) : 0;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
 #pragma unroll
@@ -143,10 +163,12 @@ __global__ __launch_bounds__(kBlock) void fused_regq(KernelArgs a) {
       }
       const float total = wave_reduce_transposed<V>(acc, lane, OpSum());
       store_group<COS, R>(s, total, lane, k0, r0, r1);
+      k0 = drawn ? r0 + next * R : k0 + nwaves * R;
     }
     CS_PHASE(1);
     __syncthreads();
     CS_PHASE(2);
+    if (drawn && tid == 0) s.next_group = nwaves;  // every draw of this slice has returned
     if (wave == 0) {
       float zfac = a.zscale;
       if (COS || (a.cosine && a.staged_norms != nullptr)) {
@@ -325,15 +347,27 @@ __global__ void zero_bytes(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Launch selection.
 
-template <bool COS, int NV, int R, bool NT, int MODE>
-hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+template <bool COS, int NV, int R, bool NT, int MODE, bool DRAWN>
+void launch_regq_drawn(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
   const bool full = (a.D >> 2) == NV * kWave;
   if (full)
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT, MODE>), dim3(ls.grid), dim3(ls.block),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT, MODE>), dim3(ls.grid),
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, true, NT, MODE, DRAWN>), dim3(ls.grid),
                        dim3(ls.block), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fused_regq<COS, NV, R, false, NT, MODE, DRAWN>), dim3(ls.grid),
+                       dim3(ls.block), 0, stream, a);
+}
+
+template <bool COS, int NV, int R, bool NT, int MODE>
+hipError_t launch_regq_nv(const KernelArgs& a, const LaunchShape& ls, hipStream_t stream) {
+  if constexpr (MODE == kRagged)
+    launch_regq_drawn<COS, NV, R, NT, MODE, true>(a, ls, stream);
+  else if constexpr (MODE == kRaggedSplit)
+    launch_regq_drawn<COS, NV, R, NT, MODE, false>(a, ls, stream);
+  else if (a.G == 1)
+    launch_regq_drawn<COS, NV, R, NT, MODE, true>(a, ls, stream);
+  else
+    launch_regq_drawn<COS, NV, R, NT, MODE, false>(a, ls, stream);
   return hipGetLastError();
 }
 

@@ -683,6 +683,10 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
   // fp32 kernels.
   const int G = a.G;
   const long long items = (long long)a.B * G;
+  // Unsplit questions take their row groups from the LDS counter, slices of
+  // a split question a fixed share (as in the fp32 kernels).
+  const bool drawn = G == 1;
+  if (tid == 0) s.next_group = nwaves;
   for (long long item = blockIdx.x; item < items; item += gridDim.x) {
     const int b = (int)(item / G), g = (int)(item % G);
     const Question qn{(size_t)b * (size_t)a.K, a.K};
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
 #ifdef CS_PHASE_CLOCKS
     int quarter = 1;
 #endif
-    for (int k0 = r0 + wave * R; k0 < r1; k0 += nwaves * R) {
+    for (int k0 = r0 + wave * R; k0 < r1;) {
 #ifdef CS_PHASE_CLOCKS
       if (quarter <= 3 && 4 * (k0 - r0) >= quarter * (r1 - r0)) {
         CS_PHASE_IN(3, 1 + quarter);
@@ -726,6 +730,7 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
           c[r][j] = (FULL || idx < pieces) ? load_piece<NT>(rows[r] + 8 * idx)
                                            : make_uint4(0u, 0u, 0u, 0u);
       }
+      const int next = drawn ? draw_group(s, lane) : 0;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const float4 u0 = us_lo[lane + kWave * j], u1 = us_hi[lane + kWave * j];
@@ -735,8 +740,10 @@ __global__ __launch_bounds__(kBlock) void fused_bf16_dot(KernelArgs a,
       }
       const float total = wave_reduce_transposed<R>(acc, lane, OpSum());
       store_group<false, R>(s, total, lane, k0, r0, r1);
+      k0 = drawn ? r0 + next * R : k0 + nwaves * R;
     }
     __syncthreads();
+    if (drawn && tid == 0) s.next_group = nwaves;  // every draw of this slice has returned
     if (wave == 0) slice_softmax<false>(s, a, qn, b, g, r0, r1 - r0, a.zscale, lane, G);
     if (G > 1) split_merge(s, a, qn, b, tid, lane, wave, G);
     __syncthreads();
