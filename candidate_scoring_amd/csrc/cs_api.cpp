@@ -218,6 +218,7 @@ cs::LaunchShape make_shape(int B, int K, int D, int G, int rpg, const void* Q, c
   const int waves = std::max(1, std::min(max_waves, (rpg + rows_per_wave - 1) / rows_per_wave));
   ls.block = (unsigned)(waves * kWave);
   ls.grid = (unsigned)std::min<long long>((long long)B * G, kGridCap);
+  ls.units = device_compute_units();
   return ls;
 }
 
@@ -470,6 +471,17 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   return CS_OK;
 }
 
+// The fields of a dense call that the launch selection reads.
+cs::KernelArgs plan_args(int B, int K, int D, int G, int similarity) {
+  cs::KernelArgs a{};
+  a.B = B;
+  a.K = K;
+  a.D = D;
+  a.G = G;
+  a.cosine = similarity == CS_SIM_COSINE;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,7 +523,8 @@ int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int a
   // 16-byte aligned or deliberately misaligned dummy addresses
   const void* p = reinterpret_cast<const void*>(uintptr_t(aligned16 ? 256 : 260));
   const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, p, p);
-  if (grid) *grid = ls.grid;
+  const unsigned persistent = cs::stream_grid(plan_args(B, K, D, G, similarity), ls);
+  if (grid) *grid = persistent > 0 ? persistent : ls.grid;
   if (block) *block = ls.block;
   if (groups) *groups = G;
   return CS_OK;
@@ -526,11 +539,18 @@ int cs_plan_kernel(int B, int K, int D, int similarity, int has_workspace, int a
   const int rpg = (K + G - 1) / G;
   const void* p = reinterpret_cast<const void*>(uintptr_t(aligned16 ? 256 : 260));
   const cs::LaunchShape ls = make_shape(B, K, D, G, rpg, p, p);
+  const unsigned persistent = cs::stream_grid(plan_args(B, K, D, G, similarity), ls);
   const char* sim = similarity == CS_SIM_COSINE ? "cosine" : "dot";
   const char* nt = ls.nt ? "non-temporal" : "cached";
   const char* mode = G > 1 ? "split" : "one workgroup per question";
   int n;
-  if (ls.nv > 0)
+  if (persistent > 0)
+    n = snprintf(name, name_bytes,
+                 "fused_regq_stream<%s, %d pieces/lane, %d rows/wave, %s, %s, %u workgroups over "
+                 "the questions>",
+                 sim, ls.nv, cs::regq_rows_per_wave(ls.nv),
+                 D / 4 == ls.nv * 64 ? "full" : "partial", nt, persistent);
+  else if (ls.nv > 0)
     n = snprintf(name, name_bytes, "fused_regq<%s, %d pieces/lane, %d rows/wave, %s, %s, %s>",
                  sim, ls.nv, cs::regq_rows_per_wave(ls.nv),
                  D / 4 == ls.nv * 64 ? "full" : "partial", nt, mode);

@@ -35,7 +35,14 @@ struct LaunchShape {
   int nv;          // > 0: register-query kernel with this many 16-byte pieces per lane
   int vec;         // general kernel: 4 (16-byte pieces) or 1 (scalar)
   int nt;          // 1: load candidates non-temporally (streamed, larger than L2)
+  int units;       // compute units of the device (persistent grids); 0 if unknown
 };
+
+// Workgroups of the persistent kernel that a dense, unsplit call with this
+// shape launches (a.B, a.K, a.D, a.G, a.cosine, a.offsets, a.staged_norms
+// are read); 0 when it launches one workgroup per question instead (few or
+// short questions, no device to ask, or another path).
+unsigned stream_grid(const KernelArgs& a, const LaunchShape& ls);
 
 // Rows per wave of the register-query kernel for a given nv.
 int regq_rows_per_wave(int nv);

@@ -122,18 +122,24 @@ int cs_workspace_init(void *workspace, size_t bytes, hipStream_t stream);
  * count depends on the current device's compute-unit count. */
 int cs_plan_groups(int B, int K, int D, int similarity, int has_workspace);
 
-/* The launch cs_score_candidates_batch() would make for these sizes: grid
- * (workgroups), block (threads) and workgroups per question, for pointers
- * that are (aligned16 != 0) or are not 16-byte aligned. Returns CS_OK or a
- * size-validation status. For benches that time a matching empty kernel:
- * the launch-bound floor of "What it is worth", graph paragraph. */
+/* The launch cs_score_candidates_batch() would make for these sizes on the
+ * current device: grid (workgroups), block (threads) and workgroups per
+ * question, for pointers that are (aligned16 != 0) or are not 16-byte
+ * aligned. A dense batch of more questions than compute units, one
+ * workgroup per question, of 64 candidates or more each, runs a persistent
+ * grid of the workgroups the device holds at once; without a device to
+ * ask, grid is the
+ * one-workgroup-per-question count. Returns CS_OK or a size-validation
+ * status. For benches that time a matching empty kernel: the launch-bound
+ * floor of "What it is worth", graph paragraph. */
 int cs_plan_launch(int B, int K, int D, int similarity, int has_workspace, int aligned16,
                    unsigned *grid, unsigned *block, int *groups);
 
 /* Writes to name (name_bytes long, NUL-terminated) a description of the
  * kernel instantiation cs_score_candidates_batch() launches for these sizes:
  * kernel, similarity, pieces per lane and rows per wave, cached or
- * non-temporal loads, split or not. For reports that label measurements
+ * non-temporal loads, split, one workgroup per question, or a persistent
+ * grid (as cs_plan_launch() decides). For reports that label measurements
  * by the code that ran. Returns CS_OK, a size-validation status,
  * CS_ERR_NULL_POINTER, or CS_ERR_WORKSPACE if name_bytes is too short. */
 int cs_plan_kernel(int B, int K, int D, int similarity, int has_workspace, int aligned16,

@@ -262,6 +262,7 @@ def test_plan_queries_name_the_launch(lib):
     bench labels its roofline with it); both plan queries return the
     argument checks' status for invalid sizes."""
     st, name = cs.cs_plan_kernel(1024, 255, 2560, "dot", True)
+    # with no device to ask for the persistent grid: one workgroup per question
     assert st == 0 and name.startswith("fused_regq<dot, 10 pieces/lane, 2 rows/wave, full")
     assert "non-temporal" in name and "one workgroup per question" in name
     st, name = cs.cs_plan_kernel(1, 255, 512, "cosine", True)

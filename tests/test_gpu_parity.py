@@ -399,14 +399,47 @@ def test_unfused_general_shapes(cs, orc, dev, D, offset):
         check(out.cpu().numpy(), want, f"unfused D={D} {sim}")
 
 
+@pytest.mark.parametrize("B,K,D,sim", [
+    (300, 255, 2560, "dot"),    # 256 workgroups: 44 of them take a second question
+    (600, 255, 512, "cosine"),  # several workgroups per compute unit
+    (513, 255, 1000, "cosine"), # pieces past D: the partial instantiation
+    (20000, 64, 64, "cosine"),  # dozens of questions per workgroup
+    (3000, 64, 4, "dot"),       # the fewest rows that take the persistent grid
+    (257, 130, 2560, "dot"),    # one question more than compute units
+])
+def test_persistent_batches(cs, orc, dev, B, K, D, sim):
+    """Dense batches of more questions than compute units run the persistent
+    grid, whose workgroups walk questions b, b + grid, ... and issue the next
+    question's first loads before the current softmax; every element is
+    checked against the oracle."""
+    st, grid, block, groups = cs.cs_plan_launch(B, K, D, sim, False)
+    assert st == 0 and groups == 1 and grid <= B, (st, grid, groups)
+    st, name = cs.cs_plan_kernel(B, K, D, sim, False)
+    assert st == 0 and name.startswith("fused_regq_stream<") and grid < B, name
+    Q, C = workloads.normal_inputs(160 + B, B, K, D)
+    scale = 14.285714 if sim == "cosine" else 0.0625
+    note(f"case persistent B={B} K={K} D={D} {sim} grid={grid} block={block}")
+    p = run(cs, Q, C, sim, scale, 1.0, dev, "batch", groups=1)
+    check(p, orc.score(Q, C, sim, scale), f"persistent B={B} K={K} D={D} {sim}")
+
+
+def test_short_questions_keep_one_workgroup_each(cs):
+    """Questions of fewer than 64 candidates stay on one workgroup per
+    question, however many there are."""
+    st, grid, block, groups = cs.cs_plan_launch(40000, 63, 256, "dot", False)
+    assert st == 0 and grid == 40000 and groups == 1
+    st, name = cs.cs_plan_kernel(40000, 63, 256, "dot", False)
+    assert st == 0 and name.startswith("fused_regq<") and name.endswith("one workgroup per question>")
+
+
 @pytest.mark.parametrize("sim", ["dot", "cosine"])
 def test_batch_beyond_the_grid_cap(cs, orc, dev, sim):
     """More questions than the launch's grid cap (2^20 workgroups): the
-    workgroups stride over the remaining questions. Every element is checked
-    against the oracle."""
+    persistent grid's workgroups walk the questions. Every element is
+    checked against the oracle."""
     B, K, D = (1 << 20) + 37, 3, 4
     st, grid, block, groups = cs.cs_plan_launch(B, K, D, sim, False)
-    assert st == 0 and grid == 1 << 20 and groups == 1, (st, grid, groups)
+    assert st == 0 and grid <= 1 << 20 and groups == 1, (st, grid, groups)
     Q, C = workloads.normal_inputs(120 if sim == "dot" else 121, B, K, D)
     note(f"case grid cap B={B} K={K} D={D} {sim} grid={grid} block={block}")
     p = run(cs, Q, C, sim, 2.0, 1.0, dev, "batch", groups=1)
