@@ -23,7 +23,8 @@ def note(msg):
 
 
 CASES = [("clm_cos_255x512", True), ("clm_cos_255x512", False), ("kev_dot_255x2560", True),
-         ("clm_cos_batch8_255x512", True), ("clm_cos_5x512", True)]
+         ("clm_cos_batch8_255x512", True), ("clm_cos_5x512", True),
+         ("kev_dot_batch1024_255x2560", False)]  # the persistent grid
 
 
 @pytest.mark.parametrize("name,use_ws", CASES)
