@@ -461,21 +461,30 @@ void launch_regq_drawn(const KernelArgs& a, const LaunchShape& ls, hipStream_t s
 }
 
 // Workgroups of fused_regq_stream<COS, NV, R, FULL, NT> with `block` threads
-// that one compute unit holds at once (cached per instantiation and block
-// size); 0 when the runtime cannot tell (no device).
+// that one compute unit of the current device holds at once (cached per
+// instantiation, device and block size); 0 when the runtime cannot tell
+// (no device).
 template <bool COS, int NV, int R, bool FULL, bool NT>
 int stream_resident(unsigned block) {
-  static std::atomic<int> cached[kBlock / kWave + 1];
+  constexpr int kDevices = 64, kSlots = kBlock / kWave + 1;
+  static std::atomic<int> cached[kDevices][kSlots];
   const unsigned slot = block / kWave;
-  if (slot > (unsigned)(kBlock / kWave)) return 0;
-  int n = cached[slot].load(std::memory_order_relaxed);
-  if (n > 0) return n;
+  int dev = 0;
+  if (slot >= (unsigned)kSlots || hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < kDevices) {
+    const int n = cached[dev][slot].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &n, fused_regq_stream<COS, NV, R, FULL, NT>, (int)block, 0) != hipSuccess || n <= 0) {
     (void)hipGetLastError();
     return 0;
   }
-  cached[slot].store(n, std::memory_order_relaxed);
+  if (dev < kDevices) cached[dev][slot].store(n, std::memory_order_relaxed);
   return n;
 }
 
