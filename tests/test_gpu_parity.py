@@ -423,6 +423,21 @@ def test_persistent_batches(cs, orc, dev, B, K, D, sim):
     check(p, orc.score(Q, C, sim, scale), f"persistent B={B} K={K} D={D} {sim}")
 
 
+def test_persistent_identical_rows_give_exactly_one_over_k(cs, dev):
+    """Identical candidates on the persistent grid: whichever wave draws a
+    row group, every row goes through the same reduction, so each
+    probability is exactly fp32(1/K) (the drawn row groups keep this)."""
+    B, K, D = 2000, 255, 512
+    rng = np.random.default_rng(171)
+    Q = rng.standard_normal((B, D), dtype=np.float32)
+    C = np.repeat(rng.standard_normal((B, 1, D), dtype=np.float32), K, axis=1)
+    st, grid, block, groups = cs.cs_plan_launch(B, K, D, "cosine", False)
+    assert st == 0 and grid < B
+    note(f"case persistent identical rows B={B} K={K} D={D} grid={grid}")
+    p = run(cs, Q, C, "cosine", 14.285714, 1.0, dev, "batch", groups=1)
+    assert np.all(p == np.float32(1.0 / K))
+
+
 def test_short_questions_keep_one_workgroup_each(cs):
     """Questions of fewer than 64 candidates stay on one workgroup per
     question, however many there are."""
