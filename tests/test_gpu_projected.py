@@ -102,6 +102,8 @@ def dev(cs):
                                            # resident; partial pieces per lane
     (1025, 255, 64, 512, 64, "dot"),       # 32 question blocks and one more
     (1024, 1, 8, 8, 8, "dot"),             # one row per question: most waves get none
+    (600, 100, 64, 512, 64, "dot"),        # more than two questions per compute unit
+    (1031, 255, 64, 1000, 96, "dot"),      # the same with partial pieces per lane
 ])
 def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
     w = workloads.projected_inputs(70 + B + K + P, B, K, Hq, Hc, P, sim)
