@@ -1140,7 +1140,7 @@ __device__ __forceinline__ void stage_fill(const uint16_t* Xb, const uint16_t* w
 // base (an address inside one stage tile).
 template <int N>
 __device__ __forceinline__ void lds_blocks(bf16x8_t (&f)[N], const uint8_t* base) {
-  static_assert(N >= 1 && N <= 4, "blocks per step");
+  static_assert(N >= 1 && N <= 8, "blocks per step");
 #pragma unroll
   for (int i = 0; i < N; ++i)
     f[i] = *reinterpret_cast<const bf16x8_t*>(base + i * 32 * kARowBytes);
@@ -1155,9 +1155,9 @@ struct StageOffsets {
 };
 
 template <int TN, int RB>
-__device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int wcb) {
+__device__ __forceinline__ StageOffsets stage_offsets(int lane, int wr, int col0) {
   StageOffsets o;
-  const int rx = 32 * RB * wr + (lane & 31), rw = 32 * TN * wcb + (lane & 31);
+  const int rx = 32 * RB * wr + (lane & 31), rw = col0 + (lane & 31);
 #pragma unroll
   for (int ks = 0; ks < kAKSteps; ++ks) {
     const int piece = 2 * ks + (lane >> 5);
@@ -1206,7 +1206,7 @@ template <int S, int TN, int RB, bool NT>
 __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageOffsets& o,
                                            const uint16_t* Xb, const uint16_t* Xn,
                                            const uint16_t* wc, int c, int nchunks, int K, int H,
-                                           int wave, int lane) {
+                                           int wave, int lane, int P) {
   if (c >= nchunks) return;
   if (c >= 0) {
     // With two stages the only chunk in flight is c itself (issued at the
@@ -1225,7 +1225,7 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageO
   // matrix core is not idle while the DMA instructions queue for the memory
   // pipeline (all eight waves issuing measured 3-5 % slower).
   if (next >= 0 && src != nullptr && wave < kDmaWaves)
-    stage_fill<(S + kAStages - 1) % kAStages, 256 / kDmaWaves, NT>(src, wc, next, K, 64 * TN, H,
+    stage_fill<(S + kAStages - 1) % kAStages, 256 / kDmaWaves, NT>(src, wc, next, K, P, H,
                                                                    wave, lane);
   if (c >= 0) stage_mfma<S, TN, RB>(acc, o);
 }
@@ -1242,13 +1242,13 @@ __device__ __forceinline__ void qp_fill(const float* qrow, int P, int lane) {
 // vector-memory counter) and barriers that do not wait for the next
 // question's DMAs already in flight. The ring's last wait covered the q' DMA,
 // which wave 0 issued before the question's later chunks.
-template <int TN, int RB>
+template <int TN, int RB, int PT>
 __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
                                                   const f32x16_t (&acc)[RB][TN], int b, int K,
-                                                  int lane, int wave, int wr, int wcb) {
+                                                  int lane, int wave, int wr, int wcb, int col0) {
   float qv[TN];
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) qv[tn] = g_qp[32 * TN * wcb + 32 * tn + (lane & 31)];
+  for (int tn = 0; tn < TN; ++tn) qv[tn] = g_qp[col0 + 32 * tn + (lane & 31)];
   // Accumulator e of tile (rb, tn) in lane l holds C'[row][col] with
   // row = 32*RB*wr + 32*rb + 8*(e/4) + 4*(l/32) + e%4 and
   // col = 32*TN*wcb + 32*tn + l%32; pairs of row blocks are reduced at once.
@@ -1293,12 +1293,12 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
   }
   stage_barrier();
   if (wave == 0) {
-    float qpv[TN];
+    float qpv[PT];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) qpv[i] = g_qp[lane + kWave * i];
+    for (int i = 0; i < PT; ++i) qpv[i] = g_qp[lane + kWave * i];
     float qq = 0.0f;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) qq = fmaf(qpv[i], qpv[i], qq);
+    for (int i = 0; i < PT; ++i) qq = fmaf(qpv[i], qpv[i], qq);
     qq = wave_allreduce(qq, lane, OpSum());
     const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
     const Question qn{(size_t)b * (size_t)K, K};
@@ -1311,20 +1311,20 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
 // A workgroup takes questions blockIdx.x, blockIdx.x + gridDim.x, ... and,
 // when the chunk count is even, keeps the ring running across them: the first
 // chunk of the next question is in flight during the last step and the
-// epilogue of the current one. RB = 2: 8 waves, each 64 rows x 32*TN
-// features; RB = 4: 4 waves, each 128 rows x 32*TN features (fewer fragment
-// reads per matrix instruction, one wave per SIMD).
-template <int TN, bool NT, int RB>
-__global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
-    KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
-    const float* __restrict__ qp) {
-  static_assert(kAStages == 2, "the chunk loop is unrolled by the stage count");
-  static_assert(RB == 2 || RB == 4, "row blocks per wave");
-  constexpr int kRowGroups = 8 / RB;
-  __shared__ Lds s;
-  constexpr int P = 64 * TN;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wr = wave % kRowGroups, wcb = wave / kRowGroups;
+// epilogue of the current one. 8 waves; wave w owns rows 64 (w % 4) .. +64
+// (RB = 2 row blocks of 32) and a run of TNW 32-feature column blocks
+// starting at feature col0. The two waves of a SIMD share its matrix core,
+// and the one that issues the chunk's DMAs (waves 0-3, stalled while the
+// requests queue) takes TN - 1 of the question's 2 TN column blocks, the
+// other TN + 1: with TN each, the 1024-question CLM batch took 84.7 us
+// (kernel trace) against 81.3 us, and a 2 / 6 split spills.
+template <int TNW, int PT, bool NT, int RB>
+__device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
+                                              const uint16_t* __restrict__ xc,
+                                              const uint16_t* __restrict__ wc,
+                                              const float* __restrict__ qp, int wave, int lane,
+                                              int wr, int wcb, int col0) {
+  constexpr int P = 64 * PT;
   const int H = a.D, K = a.K;
   const int nchunks = H / kAChunk;
   // The host launches this kernel for H >= 64 only. Knowing that the chunk
@@ -1334,26 +1334,45 @@ __global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
   __builtin_assume(nchunks >= 1);
   const bool carry = nchunks % kAStages == 0;
   const int stride = (int)gridDim.x;
-  const StageOffsets o = stage_offsets<TN, RB>(lane, wr, wcb);
+  const StageOffsets o = stage_offsets<TNW, RB>(lane, wr, col0);
   for (int b = blockIdx.x; b < a.B; b += stride) {
     const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
     const uint16_t* Xn =
         (carry && b + stride < a.B) ? xc + (size_t)(b + stride) * (size_t)K * (size_t)H : nullptr;
     if (wave == 0) qp_fill(qp + (size_t)b * P, P, lane);
-    f32x16_t acc[RB][TN];
+    f32x16_t acc[RB][TNW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
+      for (int tn = 0; tn < TNW; ++tn)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
     if (!carry || b == (int)blockIdx.x)
-      stage_step<1, TN, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane);
+      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane, P);
     for (int c = 0; c < nchunks; c += kAStages) {
-      stage_step<0, TN, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane);
-      stage_step<1, TN, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane);
+      stage_step<0, TNW, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane, P);
+      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane, P);
     }
-    cos_epilogue_ring<TN, RB>(s, a, acc, b, K, lane, wave, wr, wcb);
+    cos_epilogue_ring<TNW, RB, PT>(s, a, acc, b, K, lane, wave, wr, wcb, col0);
+  }
+}
+
+template <int TN, bool NT, int RB>
+__global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
+    KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
+    const float* __restrict__ qp) {
+  static_assert(kAStages == 2, "the chunk loop is unrolled by the stage count");
+  static_assert(RB == 2, "row blocks per wave");
+  __shared__ Lds s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wr = wave % 4, wcb = wave / 4;
+  if constexpr (TN >= 2) {
+    if (wcb == 0)
+      cos_ring_role<TN - 1, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, 0, 0);
+    else
+      cos_ring_role<TN + 1, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, 1, 32 * (TN - 1));
+  } else {
+    cos_ring_role<TN, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, wcb, 32 * TN * wcb);
   }
 }
 
