@@ -51,9 +51,6 @@ constexpr double kSliceScale = 1.2;
 // question that one 8-wave workgroup streams in less than that (about
 // 160 GB/s x 2 us = 320 KB) is never split.
 constexpr double kMinSplitBytes = 320.0 * 1024;
-// Ragged batches with more questions than this (about one per CU) are
-// dispatched longest-first.
-constexpr int kResidentQuestions = 256;
 // Longest-first scheduling: offsets bytes per workgroup at most 1/32 of a
 // mean question's candidate bytes.
 constexpr double kRankCostRatio = 32.0;
@@ -347,12 +344,12 @@ int score_ragged(const float* Q, const float* C, const long long* offsets, int B
   a.offsets = offsets;
   a.total_rows = total_rows;
   a.status = status;
-  // More questions than resident workgroups (two 8-wave workgroups per CU):
+  // More questions than resident workgroups (one 8-wave workgroup per CU):
   // hand out the largest questions first so the batch ends evenly. Deriving
   // that order costs every workgroup one pass over the B+1 offsets, so it is
   // used only while that pass is small next to a question's own rows.
   const double mean_question_bytes = 4.0 * (double)total_rows / (double)B * (double)D;
-  a.longest_first = (!split && B > kResidentQuestions &&
+  a.longest_first = (!split && B > planning_compute_units() &&
                      8.0 * (double)B * kRankCostRatio <= mean_question_bytes)
                         ? 1
                         : 0;
