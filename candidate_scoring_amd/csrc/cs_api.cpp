@@ -442,8 +442,7 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   // the tile kernel (one workgroup per question, the next question's loads
   // in flight) wins beyond that. The query projection zeroes the tickets
   // first, so the workspace needs no preparation by the caller.
-  const int ncu = device_compute_units();
-  const int cus = ncu > 0 ? ncu : 256;
+  const int cus = planning_compute_units();
   const int cos_slices = (K + cs::kCosSliceRows - 1) / cs::kCosSliceRows;
   const long long slice_groups = (long long)B * cos_slices;
   p.cos_slice =
@@ -459,7 +458,7 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.zscale = (float)((double)scale / (double)temperature);
   p.cosine = sim == CS_SIM_COSINE;
   p.nt = 2.0 * (double)B * (double)K * (double)Hc >= kStreamBytes ? 1 : 0;
-  p.compute_units = device_compute_units();
+  p.compute_units = planning_compute_units();
   const hipError_t err = cs::launch_projected(p, stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
