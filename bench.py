@@ -361,6 +361,77 @@ def projected_phase_section(devc, calls=6, reps=12):
     return res
 
 
+def ring_phase_section(devc, calls=4, reps=8):
+    """Where the CLM cosine ring kernel's cycles go: the measurement build's
+    per-wave clocks (s_memtime) for the second question of each of the 256
+    workgroups, in the last of `calls` back-to-back calls, `reps` times.
+    Per chunk step: the vmcnt wait, the ring barrier, the DMA issue (waves
+    0-3 only), the fragment reads and matrix instructions, and the time to
+    the next step; then the epilogue's parts. Medians over workgroups, then
+    over repetitions, for the DMA-issuing waves (0-3) and the others (4-7)."""
+    torch, cs = devc.torch, devc.cs
+    lib = cs.load()
+    name = "clm_proj_cos_batch1024_255x512_p256"
+    w = workloads.make_projected(name)
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(devc.dev)
+
+    xq, xc, wq, wc = dev16(w.xq_bits), dev16(w.xc_bits), dev16(w.wq_bits), dev16(w.wc_bits)
+    out = torch.empty(w.B, w.K, dtype=torch.float32, device=devc.dev)
+    nbytes = cs.cs_projected_workspace_bytes(w.B, w.Hc, w.P, w.similarity)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=devc.dev)
+    groups, waves, slots = 256, 8, 49
+    buf = np.zeros(groups * waves * slots, dtype=np.uint64)
+    steps = ("vmcnt wait", "ring barrier", "DMA issue", "fragment reads + MFMA", "to next step")
+    epi = ("row reductions", "first barrier", "second barrier", "softmax (wave 0) / exit")
+    acc = {}
+    for _ in range(reps):
+        for _ in range(calls):
+            st = cs.cs_score_projected(xq, xc, wq, wc, w.B, w.K, w.Hq, w.Hc, w.P, w.similarity,
+                                       float(w.scale), 1.0, out, ws, nbytes, devc.stream)
+            assert st == 0, st
+        torch.cuda.synchronize()
+        if lib.cs_ring_phase_clocks_read(ctypes.c_void_p(buf.ctypes.data), buf.nbytes) != 0:
+            raise RuntimeError("cs_ring_phase_clocks_read failed")
+        T = buf.reshape(groups, waves, slots).astype(np.int64)
+        if T[:, :, 44].min() <= 0:
+            raise RuntimeError("no ring clocks recorded: the calls did not reach libcs_phase.so")
+        # cycles per 10 ns tick between the first and the third question's ends
+        ghz = np.median((T[:, :, 47] - T[:, :, 45]) / (T[:, :, 48] - T[:, :, 46])) / 10.0
+        acc.setdefault("clock GHz", []).append(ghz)
+        for role, sel in (("DMA waves 0-3", slice(0, 4)), ("waves 4-7", slice(4, 8))):
+            R = T[:, sel]
+            for c in range(8):
+                t = [R[:, :, 5 * c + k] for k in range(5)]
+                nxt = R[:, :, 5 * (c + 1)] if c < 7 else R[:, :, 40]
+                for name_, v in zip(steps, (t[1] - t[0], t[2] - t[1], t[3] - t[2], t[4] - t[3],
+                                            nxt - t[4])):
+                    acc.setdefault((role, name_), [[] for _ in range(8)])[c].append(np.median(v))
+            e = [R[:, :, 40 + k] for k in range(5)]
+            for k, name_ in enumerate(epi):
+                acc.setdefault((role, name_), []).append(np.median(e[k + 1] - e[k]))
+            acc.setdefault((role, "question"), []).append(np.median(R[:, :, 44] - R[:, :, 0]))
+        acc.setdefault("wave 0 softmax", []).append(np.median(T[:, 0, 44] - T[:, 0, 43]))
+    ghz = float(np.median(acc["clock GHz"]))
+    res = {"workload": name, "B": w.B, "K": w.K, "Hc": w.Hc, "P": w.P, "calls": calls,
+           "reps": reps, "clock_GHz": round(ghz, 3), "unit": "cycles (s_memtime)"}
+    for role in ("DMA waves 0-3", "waves 4-7"):
+        r = {}
+        for name_ in steps:
+            r[name_ + " per chunk"] = [int(round(np.median(x))) for x in acc[(role, name_)]]
+        for name_ in epi:
+            r["epilogue: " + name_] = int(round(np.median(acc[(role, name_)])))
+        q = float(np.median(acc[(role, "question")]))
+        r["question"] = int(round(q))
+        r["question us"] = round(q / ghz / 1e3, 3)
+        res[role] = r
+    res["epilogue: softmax, wave 0"] = int(round(np.median(acc["wave 0 softmax"])))
+    log(f"ring phase clocks: {res}")
+    del xq, xc, wq, wc, out, ws
+    return res
+
+
 def ab_section(devc, iters, headline=None):
     """Fused vs the unfused baseline (separate norm pass + scoring that loads
     the staged norms) on the page's results-table shapes and the Kev batch.
@@ -690,8 +761,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--phase-clocks", action="store_true",
-                    help="only the per-phase clocks of the split calls and of the Kev "
-                         "projection call, from the measurement "
+                    help="only the per-phase clocks of the split calls, of the Kev "
+                         "projection call and of the CLM cosine ring kernel, from the measurement "
                          "build candidate_scoring_amd/libcs_phase.so (python -m "
                          "candidate_scoring_amd.build --phase-clocks)")
     args = ap.parse_args()
@@ -709,12 +780,14 @@ def main():
         # rather than to libcs.so, which it names as a dependency.
         ctypes.CDLL(str(cs_pkg.PKG / "libcs_phase.so"), mode=ctypes.RTLD_GLOBAL)
         lib = cs_pkg.load(cs_pkg.PKG / "libcs_phase.so")
-        for fn in (lib.cs_phase_clocks_read, lib.cs_projected_phase_clocks_read):
+        for fn in (lib.cs_phase_clocks_read, lib.cs_projected_phase_clocks_read,
+                   lib.cs_ring_phase_clocks_read):
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
         devc = Device()
         print(json.dumps({"phase_clocks": phase_clock_section(devc),
                           "projected_phase_clocks": projected_phase_section(devc),
+                          "clm_ring_phase_clocks": ring_phase_section(devc),
                           "library": "libcs_phase.so (measurement build)"}), flush=True)
         return
 

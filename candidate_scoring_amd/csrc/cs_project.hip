@@ -1081,6 +1081,31 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_ws0[kATileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_ws1[kATileBytes];
 __shared__ __attribute__((aligned(1024))) float g_qp[256];  // q' of the current question
 
+#ifdef CS_PHASE_CLOCKS
+// Measurement build only: per-wave cycle clocks of the cosine ring kernel.
+// Record (workgroup < 256, wave) holds, for the workgroup's second question,
+// s_memtime at five points of each of its first eight chunk steps (entry,
+// after the vmcnt wait, after the barrier, after the DMA issue, after the
+// matrix work: slots 5c .. 5c+4) and at five points of its epilogue (entry,
+// after the row reductions, after the first and the second barrier, exit:
+// slots 40-44). Slots 45-48 hold s_memtime and s_memrealtime at the epilogue
+// exit of the first and the third question, which convert cycles to time.
+constexpr int kRingClkGroups = 256, kRingClkSlots = 49;
+}  // namespace
+// (Outside the anonymous namespace, so the host can copy it by symbol.)
+__device__ unsigned long long g_ring_clk[kRingClkGroups * 8 * kRingClkSlots];
+namespace {
+#define CS_RING_CLK(cond, slot, value)                                                   \
+  do {                                                                                   \
+    if ((cond) && lane == 0 && blockIdx.x < (unsigned)kRingClkGroups)                    \
+      g_ring_clk[(blockIdx.x * 8 + wave) * kRingClkSlots + (slot)] = (value);            \
+  } while (0)
+#else
+#define CS_RING_CLK(cond, slot, value) \
+  do {                                 \
+  } while (0)
+#endif
+
 // X tile (W == false) or W tile (W == true) of stage S.
 template <int S, bool W>
 __device__ __forceinline__ uint8_t* stage_tile() {
@@ -1206,13 +1231,17 @@ template <int S, int TN, int RB, bool NT>
 __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageOffsets& o,
                                            const uint16_t* Xb, const uint16_t* Xn,
                                            const uint16_t* wc, int c, int nchunks, int K, int H,
-                                           int wave, int lane, int P) {
+                                           int wave, int lane, int P, int qi) {
   if (c >= nchunks) return;
+  [[maybe_unused]] const bool clk = qi == 1 && c >= 0 && c < 8;
+  CS_RING_CLK(clk, 5 * c, __builtin_amdgcn_s_memtime());
   if (c >= 0) {
     // With two stages the only chunk in flight is c itself (issued at the
     // start of the previous step); stores issued since only add to the wait.
     wait_vmcnt<0>();
+    CS_RING_CLK(clk, 5 * c + 1, __builtin_amdgcn_s_memtime());
     stage_barrier();
+    CS_RING_CLK(clk, 5 * c + 2, __builtin_amdgcn_s_memtime());
   }
   int next = c + kAStages - 1;
   const uint16_t* src = Xb;
@@ -1227,7 +1256,9 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageO
   if (next >= 0 && src != nullptr && wave < kDmaWaves)
     stage_fill<(S + kAStages - 1) % kAStages, 256 / kDmaWaves, NT>(src, wc, next, K, P, H,
                                                                    wave, lane);
+  CS_RING_CLK(clk, 5 * c + 3, __builtin_amdgcn_s_memtime());
   if (c >= 0) stage_mfma<S, TN, RB>(acc, o);
+  CS_RING_CLK(clk, 5 * c + 4, __builtin_amdgcn_s_memtime());
 }
 
 // DMA of the current question's q' (P floats) into g_qp by one wave: lane l
@@ -1245,7 +1276,9 @@ __device__ __forceinline__ void qp_fill(const float* qrow, int P, int lane) {
 template <int TN, int RB, int PT>
 __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
                                                   const f32x16_t (&acc)[RB][TN], int b, int K,
-                                                  int lane, int wave, int wr, int wcb, int col0) {
+                                                  int lane, int wave, int wr, int wcb, int col0,
+                                                  int qi) {
+  CS_RING_CLK(qi == 1, 40, __builtin_amdgcn_s_memtime());
   float qv[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) qv[tn] = g_qp[col0 + 32 * tn + (lane & 31)];
@@ -1275,6 +1308,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
   }
   const int v = lane & 31, e = v & 15;
   const int row0 = 32 * RB * wr + 32 * (v >> 4) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  CS_RING_CLK(qi == 1, 41, __builtin_amdgcn_s_memtime());
   // The two column halves of a row are added in a fixed order.
   if (wcb == 0) {
 #pragma unroll
@@ -1284,6 +1318,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
     }
   }
   stage_barrier();
+  CS_RING_CLK(qi == 1, 42, __builtin_amdgcn_s_memtime());
   if (wcb == 1) {
 #pragma unroll
     for (int pr = 0; pr < RB / 2; ++pr) {
@@ -1292,6 +1327,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
     }
   }
   stage_barrier();
+  CS_RING_CLK(qi == 1, 43, __builtin_amdgcn_s_memtime());
   if (wave == 0) {
     float qpv[PT];
 #pragma unroll
@@ -1336,6 +1372,7 @@ __device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
   const int stride = (int)gridDim.x;
   const StageOffsets o = stage_offsets<TNW, RB>(lane, wr, col0);
   for (int b = blockIdx.x; b < a.B; b += stride) {
+    [[maybe_unused]] const int qi = (b - (int)blockIdx.x) / stride;  // clocks only
     const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
     const uint16_t* Xn =
         (carry && b + stride < a.B) ? xc + (size_t)(b + stride) * (size_t)K * (size_t)H : nullptr;
@@ -1348,12 +1385,15 @@ __device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
     if (!carry || b == (int)blockIdx.x)
-      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane, P);
+      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane, P, qi);
     for (int c = 0; c < nchunks; c += kAStages) {
-      stage_step<0, TNW, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane, P);
-      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane, P);
+      stage_step<0, TNW, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane, P, qi);
+      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane, P, qi);
     }
-    cos_epilogue_ring<TNW, RB, PT>(s, a, acc, b, K, lane, wave, wr, wcb, col0);
+    cos_epilogue_ring<TNW, RB, PT>(s, a, acc, b, K, lane, wave, wr, wcb, col0, qi);
+    CS_RING_CLK(qi == 1, 44, __builtin_amdgcn_s_memtime());
+    CS_RING_CLK(qi == 0 || qi == 2, qi == 0 ? 45 : 47, __builtin_amdgcn_s_memtime());
+    CS_RING_CLK(qi == 0 || qi == 2, qi == 0 ? 46 : 48, __builtin_amdgcn_s_memrealtime());
   }
 }
 
@@ -1560,6 +1600,12 @@ hipError_t launch_projected(const ProjArgs& p, hipStream_t stream) {
 // 1-3, same layout as cs_phase_clocks_read), copied to host memory.
 extern "C" int cs_projected_phase_clocks_read(void* dst, size_t bytes) {
   return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(cs::g_phase_clk), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+
+// The cosine ring kernel's per-wave clocks (256 x 8 records of 49 values).
+extern "C" int cs_ring_phase_clocks_read(void* dst, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(cs::g_ring_clk), bytes, 0,
                                   hipMemcpyDeviceToHost);
 }
 #endif
