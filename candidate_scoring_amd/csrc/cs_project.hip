@@ -1227,7 +1227,7 @@ __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[RB][TN], const StageO
 // the ring). The step with c < 0 only fills (the start of the ring).
 constexpr int kDmaWaves = 4;
 
-template <int S, int TN, int RB, bool NT>
+template <int S, int TN, int RB, bool NT, bool DMA>
 __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageOffsets& o,
                                            const uint16_t* Xb, const uint16_t* Xn,
                                            const uint16_t* wc, int c, int nchunks, int K, int H,
@@ -1238,7 +1238,8 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageO
   if (c >= 0) {
     // With two stages the only chunk in flight is c itself (issued at the
     // start of the previous step); stores issued since only add to the wait.
-    wait_vmcnt<0>();
+    // The other waves issue no DMA and do not wait for their stores.
+    if constexpr (DMA) wait_vmcnt<0>();
     CS_RING_CLK(clk, 5 * c + 1, __builtin_amdgcn_s_memtime());
     stage_barrier();
     CS_RING_CLK(clk, 5 * c + 2, __builtin_amdgcn_s_memtime());
@@ -1249,11 +1250,11 @@ __device__ __forceinline__ void stage_step(f32x16_t (&acc)[RB][TN], const StageO
     next -= nchunks;
     src = Xn;
   }
-  // Waves 0 .. 3 (one per SIMD) issue the chunk's DMAs, 64 rows each; the
-  // other wave of each SIMD goes straight to its matrix work, so the SIMD's
-  // matrix core is not idle while the DMA instructions queue for the memory
-  // pipeline (all eight waves issuing measured 3-5 % slower).
-  if (next >= 0 && src != nullptr && wave < kDmaWaves)
+  // Waves 0 .. 3 (one per SIMD, DMA) issue the chunk's DMAs, 64 rows each;
+  // the other wave of each SIMD goes straight to its matrix work, so the
+  // SIMD's matrix core is not idle while the DMA instructions queue for the
+  // memory pipeline (all eight waves issuing measured 3-5 % slower).
+  if (DMA && next >= 0 && src != nullptr)
     stage_fill<(S + kAStages - 1) % kAStages, 256 / kDmaWaves, NT>(src, wc, next, K, P, H,
                                                                    wave, lane);
   CS_RING_CLK(clk, 5 * c + 3, __builtin_amdgcn_s_memtime());
@@ -1277,7 +1278,7 @@ template <int TN, int RB, int PT>
 __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
                                                   const f32x16_t (&acc)[RB][TN], int b, int K,
                                                   int lane, int wave, int wr, int wcb, int col0,
-                                                  int qi) {
+                                                  int qi, bool now) {
   CS_RING_CLK(qi == 1, 40, __builtin_amdgcn_s_memtime());
   float qv[TN];
 #pragma unroll
@@ -1337,12 +1338,26 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
     for (int i = 0; i < PT; ++i) qq = fmaf(qpv[i], qpv[i], qq);
     qq = wave_allreduce(qq, lane, OpSum());
     const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
-    const Question qn{(size_t)b * (size_t)K, K};
-    slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane, a.G);
+    if (now) {
+      const Question qn{(size_t)b * (size_t)K, K};
+      slice_softmax<true>(s, a, qn, b, 0, 0, K, zfac, lane, a.G);
+    } else if (lane == 0) {
+      s.red[0] = zfac;  // for the softmax that the next question's first chunk step runs
+    }
   }
-  // No barrier here: wave 0 reaches the next question's first ring barrier
-  // only after the softmax, and s.dot / s.ss are written again only after it.
+  // No barrier here: the next question's first ring barrier orders these
+  // LDS writes before the deferred softmax reads them, and s.dot / s.ss /
+  // s.red are written again only by the next epilogue.
 }
+
+// The softmax of a workgroup's question other than its last runs on wave
+// kSoftmaxWave after that wave's share of the next question's first chunk:
+// those waves (4-7) wait ~1.4k cycles per chunk step at the next barrier,
+// while on wave 0 at the end of the epilogue the ~1.9k-cycle softmax held
+// up every wave at the next question's first barrier. The second chunk's
+// barrier then separates it from the next epilogue's writes of the row
+// sums, so questions of one chunk keep the softmax in the epilogue.
+constexpr int kSoftmaxWave = 4;
 
 // A workgroup takes questions blockIdx.x, blockIdx.x + gridDim.x, ... and,
 // when the chunk count is even, keeps the ring running across them: the first
@@ -1354,7 +1369,7 @@ __device__ __forceinline__ void cos_epilogue_ring(Lds& s, const KernelArgs& a,
 // requests queue) takes TN - 1 of the question's 2 TN column blocks, the
 // other TN + 1: with TN each, the 1024-question CLM batch took 84.7 us
 // (kernel trace) against 81.3 us, and a 2 / 6 split spills.
-template <int TNW, int PT, bool NT, int RB>
+template <int TNW, int PT, bool NT, int RB, bool DMA>
 __device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
                                               const uint16_t* __restrict__ xc,
                                               const uint16_t* __restrict__ wc,
@@ -1371,12 +1386,13 @@ __device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
   const bool carry = nchunks % kAStages == 0;
   const int stride = (int)gridDim.x;
   const StageOffsets o = stage_offsets<TNW, RB>(lane, wr, col0);
+  int pending = -1;  // question whose softmax is still to run (wave kSoftmaxWave)
   for (int b = blockIdx.x; b < a.B; b += stride) {
     [[maybe_unused]] const int qi = (b - (int)blockIdx.x) / stride;  // clocks only
     const uint16_t* Xb = xc + (size_t)b * (size_t)K * (size_t)H;
     const uint16_t* Xn =
         (carry && b + stride < a.B) ? xc + (size_t)(b + stride) * (size_t)K * (size_t)H : nullptr;
-    if (wave == 0) qp_fill(qp + (size_t)b * P, P, lane);
+    if (DMA && wave == 0) qp_fill(qp + (size_t)b * P, P, lane);
     f32x16_t acc[RB][TNW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -1385,12 +1401,18 @@ __device__ __forceinline__ void cos_ring_role(Lds& s, const KernelArgs& a,
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][tn][e] = 0.0f;
     if (!carry || b == (int)blockIdx.x)
-      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane, P, qi);
+      stage_step<1, TNW, RB, NT, DMA>(acc, o, Xb, Xn, wc, -1, nchunks, K, H, wave, lane, P, qi);
     for (int c = 0; c < nchunks; c += kAStages) {
-      stage_step<0, TNW, RB, NT>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane, P, qi);
-      stage_step<1, TNW, RB, NT>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane, P, qi);
+      stage_step<0, TNW, RB, NT, DMA>(acc, o, Xb, Xn, wc, c, nchunks, K, H, wave, lane, P, qi);
+      if (!DMA && c == 0 && wave == kSoftmaxWave && pending >= 0) {
+        const Question qn{(size_t)pending * (size_t)K, K};
+        slice_softmax<true>(s, a, qn, pending, 0, 0, K, s.red[0], lane, a.G);
+      }
+      stage_step<1, TNW, RB, NT, DMA>(acc, o, Xb, Xn, wc, c + 1, nchunks, K, H, wave, lane, P, qi);
     }
-    cos_epilogue_ring<TNW, RB, PT>(s, a, acc, b, K, lane, wave, wr, wcb, col0, qi);
+    const bool now = b + stride >= a.B || nchunks < 2;  // uniform
+    cos_epilogue_ring<TNW, RB, PT>(s, a, acc, b, K, lane, wave, wr, wcb, col0, qi, now);
+    pending = now ? -1 : b;
     CS_RING_CLK(qi == 1, 44, __builtin_amdgcn_s_memtime());
     CS_RING_CLK(qi == 0 || qi == 2, qi == 0 ? 45 : 47, __builtin_amdgcn_s_memtime());
     CS_RING_CLK(qi == 0 || qi == 2, qi == 0 ? 46 : 48, __builtin_amdgcn_s_memrealtime());
@@ -1406,13 +1428,17 @@ __global__ __launch_bounds__(64 * (16 / RB)) void proj_cos_mfma_async(
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wr = wave % 4, wcb = wave / 4;
+  static_assert(kDmaWaves == 4 && kSoftmaxWave >= 4, "waves 0-3 issue the DMAs");
   if constexpr (TN >= 2) {
     if (wcb == 0)
-      cos_ring_role<TN - 1, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, 0, 0);
+      cos_ring_role<TN - 1, TN, NT, RB, true>(s, a, xc, wc, qp, wave, lane, wr, 0, 0);
     else
-      cos_ring_role<TN + 1, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, 1, 32 * (TN - 1));
+      cos_ring_role<TN + 1, TN, NT, RB, false>(s, a, xc, wc, qp, wave, lane, wr, 1, 32 * (TN - 1));
   } else {
-    cos_ring_role<TN, TN, NT, RB>(s, a, xc, wc, qp, wave, lane, wr, wcb, 32 * TN * wcb);
+    if (wcb == 0)
+      cos_ring_role<TN, TN, NT, RB, true>(s, a, xc, wc, qp, wave, lane, wr, 0, 0);
+    else
+      cos_ring_role<TN, TN, NT, RB, false>(s, a, xc, wc, qp, wave, lane, wr, 1, 32 * TN);
   }
 }
 
