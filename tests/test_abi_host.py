@@ -53,6 +53,30 @@ def test_library_exports_every_declared_function(lib):
         assert hasattr(lib, n)
 
 
+CLOCK_READERS = ("cs_phase_clocks_read", "cs_projected_phase_clocks_read",
+                 "cs_ring_phase_clocks_read")
+
+
+def test_measurement_build_exports_the_abi_and_its_clock_readers(lib):
+    """libcs_phase.so (the same sources with CS_PHASE_CLOCKS) keeps every
+    declared entry point and adds the three clock readers the bench's
+    --phase-clocks sections call; the product library has none of them."""
+    phase = cs.PKG / "libcs_phase.so"
+    if not phase.exists():
+        pytest.skip("measurement build not built (python -m candidate_scoring_amd.build "
+                    "--phase-clocks)")
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", str(path)], capture_output=True,
+                             text=True, check=True).stdout
+        return set(re.findall(r"\sT\s(cs_\w+)", out))
+
+    in_phase, in_product = exported(phase), exported(cs.LIBRARY)
+    assert not [n for n in declared_functions() if n not in in_phase]
+    assert all(n in in_phase for n in CLOCK_READERS)
+    assert not [n for n in CLOCK_READERS if n in in_product]
+
+
 def test_bench_library_loads(lib):
     b = cs.load_bench()
     for n in ("csb_time_calls", "csb_time_graph", "csb_graph_nodes", "csb_time_empty", "csb_copy"):
