@@ -113,6 +113,8 @@ def test_projected_matches_oracle(cs, orc, dev, B, K, Hq, Hc, P, sim):
 
 @pytest.mark.parametrize("B,K,Hc,P", [
     (600, 33, 256, 128),   # even chunk count: the ring runs across questions
+    (400, 50, 128, 192),   # two chunks: a question's softmax runs in the next one's only loop pass
+    (280, 255, 128, 256),  # two chunks, full 255-row tiles
     (300, 40, 192, 64),    # three chunks: the ring restarts for every question
     (270, 10, 64, 256),    # one chunk of the ring
     (270, 12, 96, 64),     # hidden not a multiple of 64: the register-staged tile
