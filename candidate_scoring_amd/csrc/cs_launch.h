@@ -66,6 +66,8 @@ struct ProjArgs {
   float2* partials;    // workspace [B][G]: (max, sum) per slice
   int G;               // slices per question of the candidate pass (1: no split)
   int cos_slice;       // cosine: one workgroup per kCosSliceRows candidates of a question
+  int cos_parts;       // cosine slices: > 0 splits the P features into this many parts of 64
+  float* rowparts;     // workspace [B][256][cos_parts][2]: rows' (dot, |c'|^2) per part
   int B, K, Hq, Hc, P;
   float zscale;        // scale / temperature
   int cosine;
@@ -74,6 +76,9 @@ struct ProjArgs {
 };
 // Candidate rows per workgroup of the small-batch cosine kernel.
 constexpr int kCosSliceRows = 32;
+// Questions up to which a small cosine batch of split questions also splits
+// the projected features (the row partials this needs: 8 KiB per question).
+constexpr int kCosPartMaxB = 64;
 // 16-byte pieces per lane of the bf16 dot kernel for Hc (Hc % 8 == 0); 0 if
 // Hc is too large.
 int bf16_nv_for(int Hc);

@@ -1050,6 +1050,157 @@ __global__ __launch_bounds__(kCosSliceWaves * kWave) void proj_cos_slice(
 }
 
 // ---------------------------------------------------------------------------
+// Cosine for small batches whose questions are split into 32-candidate
+// slices anyway: the projected features are split too, one workgroup per
+// (question, slice, 64-feature part). A workgroup then streams 64 rows of
+// the candidate head instead of all P (a quarter for P = 256), and one
+// question of 255 candidates runs on 32 compute units instead of 8. A dot
+// and a squared norm are sums over the features, so each workgroup stores
+// its rows' (c'.q', |c'|^2) over its part; the question's last workgroup to
+// finish adds the parts in part order, forms the cosines and runs the
+// softmax of the whole question.
+constexpr int kCosPartWaves = 4;
+constexpr int kCosPartFeatures = 64;
+
+__global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
+    KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
+    const float* __restrict__ qp, float* __restrict__ rowparts, int Q) {
+  constexpr int kRows = kCosSliceRows;
+  constexpr int kF = kCosPartFeatures;
+  constexpr int kThreads = kCosPartWaves * kWave;
+  constexpr int kWPer = kF * 8 / kThreads;  // W pieces per thread per chunk
+  static_assert(kRows * 8 == kThreads && kWPer == 2, "one X and two W pieces per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][kRows * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kF * kRowStride];
+  __shared__ float red[kF / 32][kRows][2];
+  __shared__ Lds s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int H = a.D, K = a.K, P = kF * Q;
+  const int per_q = a.G * Q;  // workgroups of one question
+  const int b = (int)blockIdx.x / per_q, rem = (int)blockIdx.x % per_q;
+  const int g = rem / Q, j = rem % Q;
+  const int r0 = g * kRows, n = min(kRows, K - r0);
+  const uint16_t* Xs = xc + ((size_t)b * (size_t)K + (size_t)r0) * (size_t)H;
+  const uint16_t* Ws = wc + (size_t)(kF * j) * (size_t)H;
+  const int nchunks = (H + kChunk - 1) / kChunk;
+  // Waves 0 and 1 own the part's two 32-feature blocks; all four load.
+  const bool mma = wave < kF / 32;  // uniform per wave
+  const float qv = qp[(size_t)b * P + kF * j + ((32 * wave + (lane & 31)) & (kF - 1))];
+  // This thread's pieces of a chunk: row tid / 8 of X (clamped to the
+  // slice's last row) and rows tid / 8 + 32 i of the part's W rows, hidden
+  // piece tid % 8.
+  const int pc = tid & 7, xrow = min(tid >> 3, n - 1);
+  auto fetch = [&](int c, uint4& px, uint4 (&pw)[kWPer]) {
+    const int h = min(c * kChunk + 8 * pc, H - 8);
+    px = load_piece<false>(Xs + (size_t)xrow * (size_t)H + h);
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i)
+      pw[i] = load_piece<false>(Ws + (size_t)((tid >> 3) + 32 * i) * (size_t)H + h);
+  };
+  auto deposit = [&](int buf, int c, const uint4& px, const uint4 (&pw)[kWPer]) {
+    const uint32_t keep = c * kChunk + 8 * pc < H ? ~0u : 0u;
+    *reinterpret_cast<uint4*>(&sX[buf][(tid >> 3) * kRowStride + 8 * pc]) =
+        make_uint4(px.x & keep, px.y & keep, px.z & keep, px.w & keep);
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i)
+      *reinterpret_cast<uint4*>(&sW[buf][((tid >> 3) + 32 * i) * kRowStride + 8 * pc]) =
+          make_uint4(pw[i].x & keep, pw[i].y & keep, pw[i].z & keep, pw[i].w & keep);
+  };
+  uint4 px[kCosSliceAhead], pw[kCosSliceAhead][kWPer];
+#pragma unroll
+  for (int i = 0; i < kCosSliceAhead; ++i) fetch(min(i, nchunks - 1), px[i], pw[i]);
+  const int wrow = (32 * wave + (lane & 31)) & (kF - 1);
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  // Groups of kCosSliceAhead chunks, as in proj_cos_slice.
+  auto group = [&](auto refill, int c0) {
+    constexpr bool kRefill = decltype(refill)::value;
+#pragma unroll
+    for (int i = 0; i < kCosSliceAhead; ++i) {
+      const int c = c0 + i, buf = i & 1;
+      if (!kRefill && c >= nchunks) break;  // uniform (scalar)
+      deposit(buf, c, px[i], pw[i]);
+      __syncthreads();
+      if (kRefill) fetch(min(c + kCosSliceAhead, nchunks - 1), px[i], pw[i]);
+      if (mma) {
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 16; ++ks) {
+          const int kofs = 16 * ks + 8 * (lane >> 5);
+          const bf16x8_t af =
+              *reinterpret_cast<const bf16x8_t*>(&sX[buf][(lane & 31) * kRowStride + kofs]);
+          const bf16x8_t bw =
+              *reinterpret_cast<const bf16x8_t*>(&sW[buf][wrow * kRowStride + kofs]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
+        }
+      }
+    }
+  };
+  int c0 = 0;
+  for (; c0 + kCosSliceAhead < nchunks; c0 += kCosSliceAhead)
+    group(std::integral_constant<bool, true>(), c0);
+  group(std::integral_constant<bool, false>(), c0);
+  // Accumulator e of lane l (waves 0, 1): row 8*(e/4) + 4*(l/32) + e%4 of
+  // the slice, feature 64*j + 32*wave + l%32.
+  if (mma) {
+    float v[32];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      v[e] = acc[e] * qv;
+      v[16 + e] = acc[e] * acc[e];
+    }
+    const float tot = halfwave_reduce_transposed<32>(v, lane, OpSum());
+    const int idx = lane & 31, e = idx & 15;
+    red[wave][8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][idx >> 4] = tot;
+  }
+  __syncthreads();
+  // Wave 0 stores the rows' partials over this part: row k of question b,
+  // part j at ((b * 256 + k) * Q + j) * 2 (+1 for the squared norm).
+  float* const rq = rowparts + (size_t)b * kMaxSlots * (size_t)Q * 2;
+  if (tid < 2 * kRows) {
+    const int row = tid >> 1, kind = tid & 1;
+    if (row < n) rq[((size_t)(r0 + row) * Q + j) * 2 + kind] = red[0][row][kind] + red[1][row][kind];
+  }
+  // Wave 0 publishes its stores at agent scope (every XCD) and draws the
+  // question's ticket; the last of the question's workgroups merges.
+  if (wave == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) {
+      const unsigned t =
+          __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s.last = t == (unsigned)(per_q - 1);
+    }
+  }
+  __syncthreads();
+  if (!s.last) return;  // uniform across the workgroup
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int k = tid; k < K; k += kThreads) {
+    float d = 0.0f, q2 = 0.0f;
+    for (int jj = 0; jj < Q; ++jj) {
+      d += rq[((size_t)k * Q + jj) * 2];
+      q2 += rq[((size_t)k * Q + jj) * 2 + 1];
+    }
+    s.dot[k] = d;
+    s.ss[k] = q2;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxSlots / kWave; ++i) {
+      const int f = lane + kWave * i;
+      const float x = f < P ? qp[(size_t)b * P + f] : 0.0f;
+      qq = fmaf(x, x, qq);
+    }
+    qq = wave_allreduce(qq, lane, OpSum());
+    const float zfac = a.zscale * rsqrtf(fmaxf(qq, kNormEps2));
+    const Question qn{(size_t)b * (size_t)K, K};
+    slice_softmax<true, false>(s, a, qn, b, 0, 0, K, zfac, lane, 1);
+  }
+  if (tid == 0) __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // The same cosine tile with asynchronous staging (Hc % 64 == 0): the hidden
 // dimension moves through two LDS stages of 64 bf16 per row, filled by
 // global_load_lds_dwordx4 (no staging registers): one chunk is in flight
@@ -1503,6 +1654,13 @@ void launch_cos_tile(const KernelArgs& a, const ProjArgs& p, unsigned grid, hipS
 
 template <bool NT>
 hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t stream) {
+  if (p.cos_parts > 0) {
+    // Small batch of split questions: B * G * (P / 64) workgroups.
+    const dim3 grid((unsigned)(p.B * p.G * p.cos_parts)), block(kCosPartWaves * kWave);
+    hipLaunchKernelGGL(proj_cos_part, grid, block, 0, stream, a, p.xc, p.wc, p.qp, p.rowparts,
+                       p.cos_parts);
+    return hipGetLastError();
+  }
   if (p.cos_slice) {
     // Small batch: B * G workgroups (at most one per compute unit).
     const dim3 grid((unsigned)(p.B * p.G)), block(kCosSliceWaves * kWave);
