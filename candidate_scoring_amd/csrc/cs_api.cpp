@@ -461,14 +461,19 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
                                         cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)), cus)
                           : (p.cos_slice ? cos_slices : 1);
   // Questions split into slices are merged anyway, so their projected
-  // features are split into 64-wide parts as well: a workgroup streams
-  // 64 rows of the candidate head instead of all P. Up to half the compute
-  // units: one question of 255 x 512 -> 256 took 10.8 us against 13.2 us,
-  // four 13.2 against 14.2, but eight (256 workgroups) 17.7 against 16.0.
-  p.cos_parts = p.cos_slice && p.G > 1 && B <= cs::kCosPartMaxB &&
-                        (long long)B * p.G * (P / 64) <= cus / 2
-                    ? P / 64
-                    : 0;
+  // features are split into parts as well: a workgroup streams 64 or 128
+  // rows of the candidate head instead of all P. Up to half the compute
+  // units, 64-feature parts where they fit: one question of 255 x 512 -> 256
+  // took 10.8 us against 13.2 us, four 13.2 against 14.2 (eight, with 256
+  // workgroups, 17.7 against 16.0); else 128-feature parts: five 13.6
+  // against 15.3, eight 14.9 against 16.5.
+  p.cos_parts = 0;
+  if (p.cos_slice && p.G > 1 && B <= cs::kCosPartMaxB) {
+    if ((long long)B * p.G * (P / 64) <= cus / 2)
+      p.cos_parts = P / 64;
+    else if (P % 128 == 0 && P / 128 >= 2 && (long long)B * p.G * (P / 128) <= cus / 2)
+      p.cos_parts = P / 128;  // parts of 128 features
+  }
   p.B = B;
   p.K = K;
   p.Hq = Hq;

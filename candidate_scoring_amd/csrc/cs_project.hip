@@ -1060,16 +1060,16 @@ __global__ __launch_bounds__(kCosSliceWaves * kWave) void proj_cos_slice(
 // finish adds the parts in part order, forms the cosines and runs the
 // softmax of the whole question.
 constexpr int kCosPartWaves = 4;
-constexpr int kCosPartFeatures = 64;
 
+template <int kF>  // projected features per part: 64 or 128
 __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
     KernelArgs a, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc,
     const float* __restrict__ qp, float* __restrict__ rowparts, int Q) {
   constexpr int kRows = kCosSliceRows;
-  constexpr int kF = kCosPartFeatures;
   constexpr int kThreads = kCosPartWaves * kWave;
   constexpr int kWPer = kF * 8 / kThreads;  // W pieces per thread per chunk
-  static_assert(kRows * 8 == kThreads && kWPer == 2, "one X and two W pieces per thread");
+  static_assert(kF == 64 || kF == 128, "64 or 128 features per part");
+  static_assert(kRows * 8 == kThreads, "one X piece per thread per chunk");
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][kRows * kRowStride];
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][kF * kRowStride];
   __shared__ float red[kF / 32][kRows][2];
@@ -1083,12 +1083,12 @@ __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
   const uint16_t* Xs = xc + ((size_t)b * (size_t)K + (size_t)r0) * (size_t)H;
   const uint16_t* Ws = wc + (size_t)(kF * j) * (size_t)H;
   const int nchunks = (H + kChunk - 1) / kChunk;
-  // Waves 0 and 1 own the part's two 32-feature blocks; all four load.
+  // Waves 0 .. kF/32 - 1 own the part's 32-feature blocks; all four load.
   const bool mma = wave < kF / 32;  // uniform per wave
   const float qv = qp[(size_t)b * P + kF * j + ((32 * wave + (lane & 31)) & (kF - 1))];
   // This thread's pieces of a chunk: row tid / 8 of X (clamped to the
-  // slice's last row) and rows tid / 8 + 32 i of the part's W rows, hidden
-  // piece tid % 8.
+  // slice's last row) and rows tid / 8 + 32 i (i < kWPer) of the part's W
+  // rows, hidden piece tid % 8.
   const int pc = tid & 7, xrow = min(tid >> 3, n - 1);
   auto fetch = [&](int c, uint4& px, uint4 (&pw)[kWPer]) {
     const int h = min(c * kChunk + 8 * pc, H - 8);
@@ -1140,8 +1140,8 @@ __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
   for (; c0 + kCosSliceAhead < nchunks; c0 += kCosSliceAhead)
     group(std::integral_constant<bool, true>(), c0);
   group(std::integral_constant<bool, false>(), c0);
-  // Accumulator e of lane l (waves 0, 1): row 8*(e/4) + 4*(l/32) + e%4 of
-  // the slice, feature 64*j + 32*wave + l%32.
+  // Accumulator e of lane l (the matrix waves): row 8*(e/4) + 4*(l/32) + e%4
+  // of the slice, feature kF*j + 32*wave + l%32.
   if (mma) {
     float v[32];
 #pragma unroll
@@ -1159,7 +1159,10 @@ __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
   float* const rq = rowparts + (size_t)b * kMaxSlots * (size_t)Q * 2;
   if (tid < 2 * kRows) {
     const int row = tid >> 1, kind = tid & 1;
-    if (row < n) rq[((size_t)(r0 + row) * Q + j) * 2 + kind] = red[0][row][kind] + red[1][row][kind];
+    float sum = red[0][row][kind];
+#pragma unroll
+    for (int w = 1; w < kF / 32; ++w) sum += red[w][row][kind];
+    if (row < n) rq[((size_t)(r0 + row) * Q + j) * 2 + kind] = sum;
   }
   // Wave 0 publishes its stores at agent scope (every XCD) and draws the
   // question's ticket; the last of the question's workgroups merges.
@@ -1657,8 +1660,12 @@ hipError_t launch_cos_mfma(const KernelArgs& a, const ProjArgs& p, hipStream_t s
   if (p.cos_parts > 0) {
     // Small batch of split questions: B * G * (P / 64) workgroups.
     const dim3 grid((unsigned)(p.B * p.G * p.cos_parts)), block(kCosPartWaves * kWave);
-    hipLaunchKernelGGL(proj_cos_part, grid, block, 0, stream, a, p.xc, p.wc, p.qp, p.rowparts,
-                       p.cos_parts);
+    if (p.P / p.cos_parts == 128)
+      hipLaunchKernelGGL(proj_cos_part<128>, grid, block, 0, stream, a, p.xc, p.wc, p.qp,
+                         p.rowparts, p.cos_parts);
+    else
+      hipLaunchKernelGGL(proj_cos_part<64>, grid, block, 0, stream, a, p.xc, p.wc, p.qp,
+                         p.rowparts, p.cos_parts);
     return hipGetLastError();
   }
   if (p.cos_slice) {

@@ -66,8 +66,10 @@ def dev(cs):
 @pytest.mark.parametrize("B,K,Hq,Hc,P,sim", [
     (4, 255, 2560, 2560, 256, "dot"),      # Kev-shaped heads
     (4, 255, 512, 512, 256, "cosine"),     # CLM-shaped heads: slices x 64-feature parts
-    (5, 255, 512, 512, 256, "cosine"),     # one question more: whole-feature slices, merged
-    (8, 255, 512, 512, 256, "cosine"),     # the most split questions on whole-feature slices
+    (5, 255, 512, 512, 256, "cosine"),     # one question more: slices x 128-feature parts
+    (8, 255, 512, 512, 256, "cosine"),     # the most split questions, 128-feature parts
+    (6, 255, 64, 128, 192, "cosine"),      # P = 192 beyond 64-feature parts: whole-feature
+                                           # slices, merged
     (3, 255, 512, 512, 64, "cosine"),
     (3, 200, 256, 520, 128, "cosine"),     # hidden not a multiple of the 64-wide chunk
     (2, 64, 128, 1000, 192, "cosine"),
