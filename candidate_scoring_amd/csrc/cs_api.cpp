@@ -445,35 +445,48 @@ int score_projected(const uint16_t* xq, const uint16_t* xc, const uint16_t* wq,
   p.rowparts = p.u;
   // Small batches spread each question's candidate pass over several
   // workgroups. Dot streams 2*K*Hc bytes per question and is planned like
-  // the fp32 path. Cosine takes one workgroup per 32 candidates when the
-  // batch is small: up to one workgroup per compute unit while no question
-  // is split (K <= 32), up to a quarter of them when questions are split,
-  // since each merge costs a few microseconds of ticket round trips and
-  // the tile kernel (one workgroup per question, the next question's loads
-  // in flight) wins beyond that. The query projection zeroes the tickets
-  // first, so the workspace needs no preparation by the caller.
+  // the fp32 path. Cosine takes one workgroup per 32 candidates while the
+  // batch is small, since each merge costs a few microseconds of ticket
+  // round trips and the tile kernel (one workgroup per question, the next
+  // question's loads in flight) wins beyond that:
+  // * no question split (K <= 32): up to one workgroup per compute unit;
+  // * split questions also split the projected features into parts, so a
+  //   workgroup streams 64 or 128 rows of the candidate head instead of all
+  //   P. 64-feature parts up to half the compute units: one question of
+  //   255 x 512 -> 256 took 10.8 us against 13.2 us, four 13.2 against
+  //   14.2 (eight, with 256 workgroups, 17.7 against 16.0). Else 128-feature
+  //   parts up to three quarters of them: five questions 13.6 against 15.3,
+  //   eight 14.9 against 16.5, nine 14.8 against 16.5 on the tile kernel,
+  //   twelve 16.1-16.4 against 16.5 (sixteen, 256 workgroups, 18.7 against
+  //   16.6);
+  // * else whole-feature slices up to a quarter of the compute units.
+  // The query projection zeroes the tickets first, so the workspace needs
+  // no preparation by the caller.
   const int cus = planning_compute_units();
   const int cos_slices = (K + cs::kCosSliceRows - 1) / cs::kCosSliceRows;
   const long long slice_groups = (long long)B * cos_slices;
-  p.cos_slice =
-      sim == CS_SIM_COSINE && slice_groups <= (cos_slices == 1 ? cus : cus / 4) ? 1 : 0;
+  p.cos_slice = 0;
+  p.cos_parts = 0;
+  if (sim == CS_SIM_COSINE) {
+    const bool fits = B <= cs::kCosPartMaxB;  // the workspace holds its row partials
+    const int parts64 = P / 64, parts128 = P % 128 == 0 && P / 128 >= 2 ? P / 128 : 0;
+    if (cos_slices == 1) {
+      p.cos_slice = slice_groups <= cus ? 1 : 0;
+    } else if (fits && parts64 >= 2 && slice_groups * parts64 <= cus / 2) {
+      p.cos_slice = 1;
+      p.cos_parts = parts64;
+    } else if (fits && parts128 > 0 && slice_groups * parts128 <= 3LL * cus / 4) {
+      p.cos_slice = 1;
+      p.cos_parts = parts128;
+    } else if (slice_groups <= cus / 4) {
+      // P = 64 is a single part (the same merge); P = 192 whole-feature slices.
+      p.cos_slice = 1;
+      p.cos_parts = fits && parts64 == 1 ? 1 : 0;
+    }
+  }
   p.G = sim == CS_SIM_DOT ? plan_slices(B, K, 2.0 * (double)K * (double)Hc,
                                         cs::bf16_rows_per_wave(cs::bf16_nv_for(Hc)), cus)
                           : (p.cos_slice ? cos_slices : 1);
-  // Questions split into slices are merged anyway, so their projected
-  // features are split into parts as well: a workgroup streams 64 or 128
-  // rows of the candidate head instead of all P. Up to half the compute
-  // units, 64-feature parts where they fit: one question of 255 x 512 -> 256
-  // took 10.8 us against 13.2 us, four 13.2 against 14.2 (eight, with 256
-  // workgroups, 17.7 against 16.0); else 128-feature parts: five 13.6
-  // against 15.3, eight 14.9 against 16.5.
-  p.cos_parts = 0;
-  if (p.cos_slice && p.G > 1 && B <= cs::kCosPartMaxB) {
-    if ((long long)B * p.G * (P / 64) <= cus / 2)
-      p.cos_parts = P / 64;
-    else if (P % 128 == 0 && P / 128 >= 2 && (long long)B * p.G * (P / 128) <= cus / 2)
-      p.cos_parts = P / 128;  // parts of 128 features
-  }
   p.B = B;
   p.K = K;
   p.Hq = Hq;

@@ -67,7 +67,9 @@ def dev(cs):
     (4, 255, 2560, 2560, 256, "dot"),      # Kev-shaped heads
     (4, 255, 512, 512, 256, "cosine"),     # CLM-shaped heads: slices x 64-feature parts
     (5, 255, 512, 512, 256, "cosine"),     # one question more: slices x 128-feature parts
-    (8, 255, 512, 512, 256, "cosine"),     # the most split questions, 128-feature parts
+    (8, 255, 512, 512, 256, "cosine"),     # eight questions, 128-feature parts
+    (12, 255, 512, 512, 256, "cosine"),    # 192 workgroups: the most 128-feature parts take
+    (13, 255, 512, 512, 256, "cosine"),    # one question more: the tile kernel
     (6, 255, 64, 128, 192, "cosine"),      # P = 192 beyond 64-feature parts: whole-feature
                                            # slices, merged
     (3, 255, 512, 512, 64, "cosine"),
