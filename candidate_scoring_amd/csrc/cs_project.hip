@@ -1070,8 +1070,13 @@ __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
   constexpr int kWPer = kF * 8 / kThreads;  // W pieces per thread per chunk
   static_assert(kF == 64 || kF == 128, "64 or 128 features per part");
   static_assert(kRows * 8 == kThreads, "one X piece per thread per chunk");
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][kRows * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kF * kRowStride];
+  // LDS buffers: a batch of kStages chunks is deposited, then one barrier,
+  // then multiplied (all eight chunks of a 512-wide hidden size at once for
+  // 64-feature parts, in two batches for 128-feature ones).
+  constexpr int kStages = kF == 64 ? 8 : 4;
+  static_assert(kCosSliceAhead % kStages == 0, "whole batches per group");
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kStages][kRows * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[kStages][kF * kRowStride];
   __shared__ float red[kF / 32][kRows][2];
   __shared__ Lds s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1113,25 +1118,37 @@ __global__ __launch_bounds__(kCosPartWaves * kWave) void proj_cos_part(
   f32x16_t acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  // Groups of kCosSliceAhead chunks, as in proj_cos_slice.
+  // Groups of kCosSliceAhead chunks in registers (as in proj_cos_slice),
+  // each passed through LDS in batches of kStages chunks.
   auto group = [&](auto refill, int c0) {
     constexpr bool kRefill = decltype(refill)::value;
 #pragma unroll
-    for (int i = 0; i < kCosSliceAhead; ++i) {
-      const int c = c0 + i, buf = i & 1;
-      if (!kRefill && c >= nchunks) break;  // uniform (scalar)
-      deposit(buf, c, px[i], pw[i]);
+    for (int s0 = 0; s0 < kCosSliceAhead; s0 += kStages) {
+      if (!kRefill && c0 + s0 >= nchunks) break;  // uniform (scalar)
+      // Every wave has read the previous batch before it is overwritten.
+      if (c0 + s0 > 0) __syncthreads();
+#pragma unroll
+      for (int i = s0; i < s0 + kStages; ++i)
+        if (kRefill || c0 + i < nchunks) deposit(i - s0, c0 + i, px[i], pw[i]);
       __syncthreads();
-      if (kRefill) fetch(min(c + kCosSliceAhead, nchunks - 1), px[i], pw[i]);
+      if (kRefill) {
+#pragma unroll
+        for (int i = s0; i < s0 + kStages; ++i)
+          fetch(min(c0 + i + kCosSliceAhead, nchunks - 1), px[i], pw[i]);
+      }
       if (mma) {
 #pragma unroll
-        for (int ks = 0; ks < kChunk / 16; ++ks) {
-          const int kofs = 16 * ks + 8 * (lane >> 5);
-          const bf16x8_t af =
-              *reinterpret_cast<const bf16x8_t*>(&sX[buf][(lane & 31) * kRowStride + kofs]);
-          const bf16x8_t bw =
-              *reinterpret_cast<const bf16x8_t*>(&sW[buf][wrow * kRowStride + kofs]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
+        for (int i = s0; i < s0 + kStages; ++i) {
+          if (!kRefill && c0 + i >= nchunks) break;  // uniform (scalar)
+#pragma unroll
+          for (int ks = 0; ks < kChunk / 16; ++ks) {
+            const int kofs = 16 * ks + 8 * (lane >> 5);
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
+                &sX[i - s0][(lane & 31) * kRowStride + kofs]);
+            const bf16x8_t bw =
+                *reinterpret_cast<const bf16x8_t*>(&sW[i - s0][wrow * kRowStride + kofs]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
+          }
         }
       }
     }
