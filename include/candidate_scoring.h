@@ -253,7 +253,9 @@ int cs_plan_ragged(int B, int64_t total_rows, int D, int similarity, int has_wor
  * matrix cores and reduced to their similarity in registers. The workspace
  * (cs_projected_workspace_bytes(), 16-byte aligned) holds the projected
  * queries, the merge state of the candidate pass (which a small batch
- * spreads over several workgroups per question) and, for dot, the folded
+ * spreads over several workgroups per question; for cosine batches of up
+ * to 64 questions also each row's partial sums over parts of the projected
+ * features, 8 KiB per question) and, for dot, the folded
  * queries, an exact three-part bf16 split of the projected ones and Wc^T,
  * both in matrix-core fragment order; its contents are scratch between
  * calls (the call initialises what it needs). Implemented shapes: Hq and Hc multiples of 8, P <= 256,
