@@ -342,6 +342,11 @@ def pin_projected(orc):
             s = cosine_similarity(cv, qv[None, :])[:, 0] if sim == "cosine" else cv @ qv
             want = scipy.special.softmax(2.5 * s)
             assert np.max(np.abs(p[b] - want)) <= 1e-12, sim
+    # A zero projected query: every cosine is 0, so the distribution is
+    # exactly uniform (the same clamp as the plain path's zero query).
+    Xq0 = np.zeros_like(Xq)
+    p = orc.score_projected(Xq0, Wq, Xc, Wc, "cosine", 2.5)
+    assert np.all(p == 1.0 / K)
 
 
 PINS = [

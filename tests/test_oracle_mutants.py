@@ -47,6 +47,23 @@ MUTANTS = {
                                       "if (temperature == 0.0f || isinf(temperature))"),
     "null_query_accepted": ("if (!query_present || !candidates_present || !out_present)",
                             "if (!candidates_present || !out_present)"),
+    # ragged batches
+    "ragged_output_at_question_index": ("double *pb = p + offsets[b];", "double *pb = p + b;"),
+    "ragged_rows_of_first_question": (
+        "question_logits(Q + (size_t)b * (size_t)D, C + (size_t)offsets[b] * (size_t)D,",
+        "question_logits(Q + (size_t)b * (size_t)D, C,"),
+    "ragged_count_one_short": ("int K = (int)(offsets[b + 1] - offsets[b]);",
+                               "int K = (int)(offsets[b + 1] - offsets[b]) - 1;"),
+    # projection + scoring
+    "projected_candidate_norm_dropped": ("s = s / (qnorm * cnorm);", "s = s / qnorm;"),
+    "projected_query_norm_unclamped": ("if (qnorm < CSO_NORM_EPS) qnorm = CSO_NORM_EPS;", ""),
+    "projected_scale_dropped": ("pb[k] = (double)scale * s / (double)temperature;",
+                                "pb[k] = s / (double)temperature;"),
+    "projected_candidate_times_itself": ("double s = dot_double(c, q, P);",
+                                         "double s = dot_double(c, c, P);"),
+    "projected_query_head_for_candidates": (
+        "project(Wc, Xc + ((size_t)b * (size_t)K + (size_t)k) * (size_t)Dc, P, Dc, c);",
+        "project(Wq, Xc + ((size_t)b * (size_t)K + (size_t)k) * (size_t)Dc, P, Dc, c);"),
 }
 
 
