@@ -203,14 +203,15 @@ def test_projected_beyond_the_grid_cap(cs, orc, dev, sim):
     check(run(cs, w, dev), want(orc, w), f"grid cap {sim}")
 
 
-@pytest.mark.parametrize("B,sim", [(3, "dot"), (10, "dot"), (2, "cosine")])
+@pytest.mark.parametrize("B,sim", [(3, "dot"), (10, "dot"), (2, "cosine"), (6, "cosine"),
+                                   (10, "cosine")])
 def test_projected_split_on_an_unprepared_workspace(cs, orc, dev, B, sim):
     """A small batch spreads each question's candidate pass over several
     workgroups (dot: behind the matrix-vector and the matrix-core query side;
-    cosine: 32 candidates per workgroup), merged through tickets in the
-    workspace; the query projection clears them, so a workspace full of
-    garbage (and then the one a previous call left) gives the same correct
-    result."""
+    cosine: 32 candidates x 64 or 128 projected features per workgroup,
+    behind either query side), merged through tickets in the workspace; the
+    query projection clears them, so a workspace full of garbage (and then
+    the one a previous call left) gives the same correct result."""
     import torch
 
     H = 2560 if sim == "dot" else 512
