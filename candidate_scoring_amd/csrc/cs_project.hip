@@ -585,11 +585,14 @@ __global__ __launch_bounds__(256) void proj_query_gemv(const uint16_t* __restric
 }
 
 // u[b][h] = sum_p q'[b][p] Wc[p][h]: a workgroup takes kFoldGemvCols columns
-// (eight 16-byte pieces of every row) and all P <= 256 rows as 32 row phases;
-// the lane of phase r loads rows r, r + 32, ... in one round, multiplies them
+// (four 16-byte pieces of every row) and all P <= 256 rows as 64 row phases;
+// the lane of phase r loads rows r, r + 64, ... in one round, multiplies them
 // by q' staged in LDS, and the phases are then added in order through LDS
 // (padded so that neither the stores nor the column sums collide on a bank).
-constexpr int kFoldGemvCols = 64;
+// With 64 columns per workgroup (40 workgroups for 2560 columns) eight
+// questions took 21.3 us per call against 20.2 us with 32, four 16.0 against
+// 15.6; 16 columns gave nothing more and one question 0.4 us less.
+constexpr int kFoldGemvCols = 32;
 constexpr int kFoldGemvPieces = kFoldGemvCols / 8;
 constexpr int kFoldGemvPhases = 256 / kFoldGemvPieces;
 constexpr int kFoldGemvRows = 256 / kFoldGemvPhases;  // rows per lane at P = 256
@@ -644,11 +647,12 @@ __global__ __launch_bounds__(256) void fold_query_gemv(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) red[b][j][ph][pc] = acc[b][j];
   __syncthreads();
-  // Output o (threads take o = t, t + 256, ...) is column 8 * (o % 8) +
-  // (o / 8) % 8 of question o / 64.
+  // Output o (threads take o = t, t + 256, ...) is column
+  // 8 * (o % kFoldGemvPieces) + (o / kFoldGemvPieces) % 8 of question
+  // o / kFoldGemvCols.
 #pragma unroll
-  for (int o = tid; o < NB * 64; o += 256) {
-    const int b = o / 64, j = (o / kFoldGemvPieces) % 8, c = o % kFoldGemvPieces;
+  for (int o = tid; o < NB * kFoldGemvCols; o += 256) {
+    const int b = o / kFoldGemvCols, j = (o / kFoldGemvPieces) % 8, c = o % kFoldGemvPieces;
     float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < kFoldGemvPhases; ++r) sum += red[b][j][r][c];
